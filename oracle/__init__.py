@@ -1,0 +1,17 @@
+"""CPU oracle for the Muon optimizer step (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The library itself never calls it, and it shares no code
+with the HIP path.
+"""
+from .muon_oracle import (  # noqa: F401
+    DEFAULT_COEFFS,
+    DEFAULT_EPS,
+    momentum_update,
+    ns_source,
+    orient_wide,
+    frobenius_normalize,
+    newton_schulz,
+    newton_schulz_blockwise,
+    muon_step,
+)

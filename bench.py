@@ -1,0 +1,217 @@
+"""Benchmark of the Muon optimizer step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one full Muon step (momentum, Newton-Schulz with five iterations,
+weight update) over every matrix of the workload, inputs resident in HBM.
+Default workload: the Kimi-K2-MoE-layer-shaped batch, 384 experts x
+(2048x7168 gate, 2048x7168 up, 7168x2048 down) = 1152 bf16 matrices.
+
+Prints one JSON line. `value` is Newton-Schulz TFLOP/s counted with the SYRK
+saving (algorithmic FLOPs: upper triangles of the two symmetric products plus
+the full B X) divided by the whole step time. `roofline` describes the
+dominant kernel (largest share of step time): algorithmic FLOPs per launch
+over its average launch duration, both taken live from HIP events that the
+library records around each of its launches on the launch stream.
+`cpu_baseline` times the CPU oracle (float32, numpy/BLAS on the host cores)
+on a bounded sample of the same matrices.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12   # dense bf16 MFMA, 2516.6 TFLOP/s
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="kimi_moe_layer")
+    p.add_argument("--workspace-gb", type=float, default=32.0)
+    p.add_argument("--pack", choices=["cost", "rr"], default="cost")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="budget of the CPU-oracle sample (0 disables it)")
+    p.add_argument("--no-phase-timing", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the CPU oracle (float32) on matrices of the workload until the
+    budget is spent; report algorithmic TFLOP/s."""
+    import numpy as np
+    from muon_newton_schulz_03_amd import accounting as acc
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()
+                       if i.get("internal_api") in ("openblas", "mkl", "blis")), default=0)
+    except Exception:
+        threads = 0
+    if not threads:
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(wl.seed)
+    shapes = list(dict.fromkeys(wl.shapes))  # distinct shapes, in order
+    flops = 0.0
+    done = []
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        r, c = shapes[i % len(shapes)]
+        G = (rng.standard_normal((r, c)) * wl.std_g).astype(np.float32)
+        M = (rng.standard_normal((r, c)) * wl.std_m).astype(np.float32)
+        W = (rng.standard_normal((r, c)) * wl.std_w).astype(np.float32)
+        t = time.perf_counter()
+        oracle.muon_step(W, G, M, lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov, iters=wl.iters,
+                         col_blocks=wl.col_blocks, dtype=np.float32)
+        el = time.perf_counter() - t
+        f = sum(acc.flops_algorithmic(*acc.wide(*v), wl.iters) for v in acc.views([(r, c)], wl.col_blocks))
+        flops += f
+        done.append((f"{r}x{c}", el))
+        i += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    busy = sum(e for _, e in done)
+    return {
+        "value": round(flops / busy / 1e12, 4),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"float32 oracle muon_step on {len(done)} matrices "
+                  f"({', '.join(sorted(set(s for s, _ in done)))}) of the same workload, "
+                  f"{busy:.1f} s of CPU time",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU path is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import muon_newton_schulz_03_amd as mu
+    from muon_newton_schulz_03_amd import accounting as acc
+    from muon_newton_schulz_03_amd.workloads import WORKLOADS, make_inputs
+
+    mu.load_library()
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mode = (mu.MUON_PACK_COST if args.pack == "cost" else mu.MUON_PACK_RR)
+    if wl.col_blocks > 1:
+        mode |= mu.MUON_NS_BLOCKWISE
+    print(f"[bench] workload {wl.name}: {len(wl.shapes)} matrices; generating inputs", file=sys.stderr,
+          flush=True)
+    W, G, M = make_inputs(wl, device=dev)
+    torch.cuda.synchronize()
+    cb = [wl.col_blocks] * len(W)
+    descs = [mu.mat_of(t, c) for t, c in zip(W, cb)]
+    full = mu.muon_workspace_size(descs, mode)
+    ws_bytes = min(full, int(args.workspace_gb * (1 << 30)))
+    ws_bytes = max(ws_bytes, mu.muon_workspace_min_size(descs, mode))
+    ws = mu.Workspace(ws_bytes, device=dev)
+    plan = mu.muon_plan_info(descs, iters=wl.iters, mode=mode, workspace_bytes=ws_bytes)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mu.muon_step(W, G, M, lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov, iters=wl.iters,
+                     mode=mode, col_blocks=cb, workspace=ws.buf[:ws_bytes])
+
+    print(f"[bench] workspace {ws_bytes / 2**30:.1f} GiB, {len(plan['chunks'])} groups; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timing = not args.no_phase_timing
+    if timing:
+        mu.muon_set_phase_timing(True)
+        mu.muon_phase_times()  # clear
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phases = mu.muon_phase_times() if timing else None
+    mu.muon_set_phase_timing(False)
+    ms_step = elapsed * 1e3 / args.steps
+    print(f"[bench] {args.steps} steps, {ms_step:.2f} ms/step", file=sys.stderr, flush=True)
+
+    f_nom, f_alg = acc.workload_flops(wl.shapes, wl.iters, wl.col_blocks)
+    g_f, a_f, b_f = acc.workload_phase_flops(wl.shapes, wl.col_blocks)
+    tflops_alg = f_alg / (ms_step * 1e-3) / 1e12
+    tflops_nom = f_nom / (ms_step * 1e-3) / 1e12
+
+    out = {
+        "metric": "Newton-Schulz TFLOP/s (SYRK-counted) and % bf16 MFMA peak; Muon step ms/layer-set",
+        "value": round(tflops_alg, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "description": wl.description,
+            "matrices": len(wl.shapes),
+            "col_blocks": wl.col_blocks,
+            "iters": wl.iters,
+            "pack": args.pack,
+            "workspace_gib": round(ws_bytes / 2**30, 2),
+            "groups": len(plan["chunks"]),
+        },
+        "tflops_nominal": round(tflops_nom, 2),
+        "pct_peak_alg": round(100 * tflops_alg / PEAK_BF16_TFLOPS, 2),
+        "pct_peak_nominal": round(100 * tflops_nom / PEAK_BF16_TFLOPS, 2),
+    }
+    if phases:
+        per_step = {k: (v[0] / args.steps, v[1] // max(args.steps, 1)) for k, v in phases.items()}
+        out["phase_ms_per_step"] = {k: round(v[0], 3) for k, v in per_step.items()}
+        out["launches_per_step"] = {k: int(v[1]) for k, v in per_step.items()}
+        ns_ms = sum(per_step[k][0] for k in ("norm", "gram", "aa", "bx"))
+        out["ns_ms_per_step"] = round(ns_ms, 3)
+        out["ns_tflops_alg"] = round(f_alg / (ns_ms * 1e-3) / 1e12, 2)
+        out["ns_pct_peak_alg"] = round(100 * out["ns_tflops_alg"] / PEAK_BF16_TFLOPS, 2)
+        flops_of = {"gram": g_f * wl.iters, "aa": a_f * wl.iters, "bx": b_f * wl.iters}
+        dom = max(("gram", "aa", "bx"), key=lambda k: per_step[k][0])
+        launches = max(per_step[dom][1], 1)
+        avg_ms = per_step[dom][0] / launches
+        fl_launch = flops_of[dom] / launches
+        ach = fl_launch / (avg_ms * 1e-3) / 1e12
+        out["roofline"] = {
+            "bound": "mfma",
+            "kernel": {"gram": "gemm_bf16_kernel<0> (SYRK Gram)", "aa": "gemm_bf16_kernel<1> (SYRK A*A + poly)",
+                       "bx": "gemm_bf16_kernel<2> (GEMM B*X + axpy)"}[dom],
+            "achieved": round(ach, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": fl_launch,
+            "avg_launch_ms": round(avg_ms, 4),
+        }
+        el_bytes = acc.elementwise_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4)
+        el_ms = per_step["prep"][0] + per_step["finish"][0]
+        out["elementwise_gbs"] = round(el_bytes / (el_ms * 1e-3) / 1e9, 1) if el_ms > 0 else None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,387 @@
+// C ABI entry points: validation, planning, and the launch sequence.
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "muon.h"
+#include "plan.h"
+
+namespace {
+
+using namespace muon;
+
+struct State {
+  hipStream_t stream = nullptr;
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  int32_t iters = 5;
+  float coeffs[3] = {3.4445f, -4.7750f, 2.0315f};
+  float eps = 1e-7f;
+  uint32_t mode = MUON_NS_FULL | MUON_PACK_COST | MUON_AA_SPLIT;
+  std::string err;
+};
+
+thread_local State g_state;
+
+// Optional per-launch event pairs (muon_set_phase_timing).
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> pool;  // 2 events per record, reused
+  std::vector<int> kinds;        // kernel kind of record i
+  ~Timing() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+thread_local Timing g_timing;
+
+enum TimedKind { kTPrep = 0, kTNorm, kTGram, kTAA, kTBX, kTFinish, kTKinds };
+
+// Runs `launch` (returning hipError_t) bracketed by events when timing is on.
+template <class F>
+hipError_t timed(int kind, hipStream_t st, F &&launch) {
+  if (!g_timing.on) return launch();
+  const size_t i = g_timing.kinds.size();
+  while (g_timing.pool.size() < 2 * (i + 1)) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return r;
+    g_timing.pool.push_back(e);
+  }
+  hipError_t r = hipEventRecord(g_timing.pool[2 * i], st);
+  if (r != hipSuccess) return r;
+  r = launch();
+  if (r != hipSuccess) return r;
+  r = hipEventRecord(g_timing.pool[2 * i + 1], st);
+  if (r != hipSuccess) return r;
+  g_timing.kinds.push_back(kind);
+  return hipSuccess;
+}
+
+muon_status fail(const Error &e) {
+  g_state.err = e.msg;
+  return e.status;
+}
+muon_status fail(muon_status s, const std::string &msg) {
+  g_state.err = msg;
+  return s;
+}
+muon_status ok() {
+  g_state.err.clear();
+  return MUON_OK;
+}
+
+bool finite3(const float *c) { return std::isfinite(c[0]) && std::isfinite(c[1]) && std::isfinite(c[2]); }
+
+struct Sources {
+  const muon_mat *data = nullptr;  // muon_ns_batched
+  const muon_mat *W = nullptr, *G = nullptr, *M = nullptr;  // muon_step
+};
+
+muon_status hip_fail(hipError_t e, const char *what) {
+  return fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Launch sequence for every group of views that fits the workspace.
+muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, float beta, int nesterov,
+                    const float coeffs[3], float eps) {
+  hipStream_t st = g_state.stream;
+  char *ws = static_cast<char *>(g_state.ws);
+  const bool bf16 = plan.bf16;
+  const int iters = plan.iters;
+  const int fin = iters & 1;
+
+  for (const Chunk &ch : plan.chunks) {
+    // per-view workspace blocks, in plan order
+    std::vector<char *> blocks;
+    blocks.reserve(ch.count);
+    for (const Segment &sg : ch.segs)
+      for (int32_t k = 0; k < sg.count; ++k) blocks.push_back(ws + sg.base + size_t(k) * sg.stride);
+
+    // grouped-launch segment descriptors
+    GemmArgs ga{};
+    ga.nseg = int32_t(ch.segs.size());
+    ga.a = coeffs[0];
+    ga.b = coeffs[1];
+    ga.c = coeffs[2];
+    ga.eps = eps;
+    ga.aa_plain = (plan.mode & MUON_AA_PLAIN) ? 1 : 0;
+    ga.remap = 1;
+    int32_t view_begin = 0;
+    for (size_t s = 0; s < ch.segs.size(); ++s) {
+      const Segment &sg = ch.segs[s];
+      const Layout L = view_layout(sg.mp, sg.np, bf16);
+      GemmSeg &g = ga.seg[s];
+      g.base = ws + sg.base;
+      g.stride = int64_t(sg.stride);
+      for (int p = 0; p < 2; ++p) {
+        g.off_xa[p] = int64_t(L.xa[p]);
+        g.off_xt[p] = int64_t(L.xt[p]);
+      }
+      g.off_ahi = int64_t(L.ahi);
+      g.off_alo = int64_t(L.alo);
+      g.off_b = int64_t(L.b);
+      g.off_bdiag = int64_t(L.bdiag);
+      g.off_part = int64_t(L.partials);
+      g.off_scale = int64_t(L.scale);
+      g.mp = int32_t(sg.mp);
+      g.np = int32_t(sg.np);
+      g.count = sg.count;
+      g.tn = int32_t(sg.np / (bf16 ? kGemmTile : kPadF32));
+      g.nparts = int32_t(L.nparts);
+      g.view_begin = view_begin;
+      view_begin += sg.count;
+    }
+    auto set_tiles = [&](bool syrk) {
+      int64_t t = 0;
+      for (size_t s = 0; s < ch.segs.size(); ++s) {
+        const int64_t per = syrk ? ch.segs[s].tiles_syrk : ch.segs[s].tiles_gemm;
+        ga.seg[s].tiles_per_view = int32_t(per);
+        ga.seg[s].tile_begin = int32_t(t);
+        t += per * ch.segs[s].count;
+      }
+      ga.total_tiles = int32_t(t);
+    };
+
+    // element-wise launches, up to kElemViewsMax views each
+    auto elem_pass = [&](bool prep) -> muon_status {
+      ElemArgs ea{};
+      ea.kind = prep ? (step ? kPrepStep : kPrepNs) : (step ? kFinishStep : kFinishNs);
+      ea.beta = beta;
+      ea.lr = lr;
+      ea.nesterov = nesterov;
+      ea.final_scale = iters == 0 ? 1 : 0;
+      int32_t tiles = 0;
+      auto flush = [&]() -> muon_status {
+        ea.total_tiles = tiles;
+        hipError_t e = timed(prep ? kTPrep : kTFinish, st, [&] { return launch_elem(ea, bf16, st); });
+        if (e != hipSuccess) return hip_fail(e, prep ? "prep launch" : "finish launch");
+        ea.nv = 0;
+        tiles = 0;
+        return MUON_OK;
+      };
+      for (int32_t k = 0; k < ch.count; ++k) {
+        const View &v = plan.views[ch.first + k];
+        const Layout L = view_layout(v.mp, v.np, bf16);
+        const size_t es = bf16 ? 2 : 4;
+        ElemView &e = ea.v[ea.nv];
+        e = ElemView{};
+        const muon_mat &mm = step ? src.M[v.mat] : src.data[v.mat];
+        e.m = static_cast<char *>(mm.data) + size_t(v.col_off) * es;
+        e.ld_m = mm.ld;
+        if (step) {
+          e.g = static_cast<const char *>(src.G[v.mat].data) + size_t(v.col_off) * es;
+          e.ld_g = src.G[v.mat].ld;
+          e.w = static_cast<char *>(src.W[v.mat].data) + size_t(v.col_off) * es;
+          e.ld_w = src.W[v.mat].ld;
+        }
+        auto rows16 = [&](const void *ptr, int64_t ld) {
+          return (reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && (size_t(ld) * es) % 16 == 0) ? 1 : 0;
+        };
+        e.vec = (step ? rows16(e.g, e.ld_g) : 0) | (rows16(e.m, e.ld_m) << 1) | (step ? rows16(e.w, e.ld_w) << 2 : 0);
+        e.blk = blocks[k];
+        const int buf = prep ? 0 : fin;
+        e.off_direct = int64_t(v.tall ? L.xt[buf] : L.xa[buf]);
+        e.off_trans = int64_t(v.tall ? L.xa[buf] : L.xt[buf]);
+        e.off_part = int64_t(L.partials);
+        e.off_scale = int64_t(L.scale);
+        e.rows = int32_t(v.rows);
+        e.cols = int32_t(v.cols);
+        e.pitch_direct = int32_t(v.tall ? v.mp : v.np);
+        e.pitch_trans = int32_t(v.tall ? v.np : v.mp);
+        int64_t tr, tcn;
+        if (prep) {  // whole padded extent, so the padding is written as zeros
+          tr = (v.tall ? v.np : v.mp) / kElemTile;
+          tcn = (v.tall ? v.mp : v.np) / kElemTile;
+        } else {
+          tr = (v.rows + kElemTile - 1) / kElemTile;
+          tcn = (v.cols + kElemTile - 1) / kElemTile;
+        }
+        e.tiles_c = int32_t(tcn);
+        e.tile_begin = tiles;
+        tiles += int32_t(tr * tcn);
+        ea.nv++;
+        if (ea.nv == kElemViewsMax) {
+          muon_status s = flush();
+          if (s != MUON_OK) return s;
+        }
+      }
+      if (ea.nv) return flush();
+      return MUON_OK;
+    };
+
+    muon_status s = elem_pass(true);
+    if (s != MUON_OK) return s;
+    hipError_t e = timed(kTNorm, st, [&] { return launch_norm_finalize(ga, ch.count, st); });
+    if (e != hipSuccess) return hip_fail(e, "norm launch");
+    for (int it = 0; it < iters; ++it) {
+      ga.src = it & 1;
+      ga.first = it == 0 ? 1 : 0;
+      set_tiles(true);
+      e = timed(kTGram, st, [&] { return launch_gemm(ga, kGram, bf16, st); });
+      if (e != hipSuccess) return hip_fail(e, "gram launch");
+      e = timed(kTAA, st, [&] { return launch_gemm(ga, kAA, bf16, st); });
+      if (e != hipSuccess) return hip_fail(e, "A*A launch");
+      set_tiles(false);
+      e = timed(kTBX, st, [&] { return launch_gemm(ga, kBX, bf16, st); });
+      if (e != hipSuccess) return hip_fail(e, "B*X launch");
+    }
+    s = elem_pass(false);
+    if (s != MUON_OK) return s;
+  }
+  return ok();
+}
+
+bool check_iters(int32_t iters, Error *err) {
+  if (iters < 0 || iters > kMaxIters) return err->set(MUON_ERR_INVALID_ARG, "iters out of range [0, 64]");
+  return true;
+}
+
+bool need_workspace(Error *err) {
+  if (!g_state.ws) return err->set(MUON_ERR_WORKSPACE, "no workspace set (muon_set_workspace)");
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_ns_batched(const muon_mat *descs, int32_t n_mats, int32_t iters, const float coeffs[3],
+                            uint32_t mode) {
+  Error err;
+  static const float kDefault[3] = {3.4445f, -4.7750f, 2.0315f};
+  const float *cf = coeffs ? coeffs : kDefault;
+  if (!validate_mode(mode, &err) || !check_iters(iters, &err)) return fail(err);
+  if (!finite3(cf)) return fail(MUON_ERR_INVALID_ARG, "coefficients must be finite");
+  if (!validate_descs(descs, n_mats, mode, "descs", &err)) return fail(err);
+  if (n_mats == 0) return ok();
+  const muon_mat *arrays[1] = {descs};
+  const bool writable[1] = {true};
+  if (!check_alias(arrays, writable, 1, n_mats, &err)) return fail(err);
+  Plan plan;
+  if (!need_workspace(&err) || !build_plan(descs, n_mats, iters, mode, g_state.ws_bytes, &plan, &err))
+    return fail(err);
+  Sources src;
+  src.data = descs;
+  return execute(plan, src, false, 0.f, 0.f, 0, cf, g_state.eps);
+}
+
+muon_status muon_step(const muon_mat *params, const muon_mat *grads, const muon_mat *moms, int32_t n_mats,
+                      float lr, float beta, int32_t nesterov) {
+  Error err;
+  const uint32_t mode = g_state.mode;
+  if (!validate_descs(params, n_mats, mode, "params", &err) || !validate_descs(grads, n_mats, mode, "grads", &err) ||
+      !validate_descs(moms, n_mats, mode, "moms", &err))
+    return fail(err);
+  if (n_mats > 0 && !validate_step_triplets(params, grads, moms, n_mats, &err)) return fail(err);
+  if (!std::isfinite(lr) || !std::isfinite(beta)) return fail(MUON_ERR_INVALID_ARG, "lr and beta must be finite");
+  if (nesterov != 0 && nesterov != 1) return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
+  if (n_mats == 0) return ok();
+  const muon_mat *arrays[3] = {params, grads, moms};
+  const bool writable[3] = {true, false, true};
+  if (!check_alias(arrays, writable, 3, n_mats, &err)) return fail(err);
+  Plan plan;
+  if (!need_workspace(&err) || !build_plan(params, n_mats, g_state.iters, mode, g_state.ws_bytes, &plan, &err))
+    return fail(err);
+  Sources src;
+  src.W = params;
+  src.G = grads;
+  src.M = moms;
+  return execute(plan, src, true, lr, beta, nesterov, g_state.coeffs, g_state.eps);
+}
+
+muon_status muon_set_stream(void *hip_stream) {
+  g_state.stream = static_cast<hipStream_t>(hip_stream);
+  return ok();
+}
+
+muon_status muon_workspace_size(const muon_mat *descs, int32_t n_mats, uint32_t mode, size_t *bytes) {
+  Error err;
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (!validate_mode(mode, &err) || !validate_descs(descs, n_mats, mode, "descs", &err)) return fail(err);
+  Plan plan;
+  if (!build_plan(descs, n_mats, 1, mode, 0, &plan, &err)) return fail(err);
+  *bytes = plan.full_bytes;
+  return ok();
+}
+
+muon_status muon_workspace_min_size(const muon_mat *descs, int32_t n_mats, uint32_t mode, size_t *bytes) {
+  Error err;
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (!validate_mode(mode, &err) || !validate_descs(descs, n_mats, mode, "descs", &err)) return fail(err);
+  Plan plan;
+  if (!build_plan(descs, n_mats, 1, mode, 0, &plan, &err)) return fail(err);
+  *bytes = plan.min_bytes;
+  return ok();
+}
+
+muon_status muon_set_workspace(void *device_ptr, size_t bytes) {
+  if ((device_ptr == nullptr) != (bytes == 0))
+    return fail(MUON_ERR_INVALID_ARG, "workspace pointer and size must both be set or both be empty");
+  if (reinterpret_cast<uintptr_t>(device_ptr) % 256) return fail(MUON_ERR_ALIGN, "workspace not 256-byte aligned");
+  g_state.ws = device_ptr;
+  g_state.ws_bytes = bytes;
+  return ok();
+}
+
+muon_status muon_set_step_options(int32_t iters, const float coeffs[3], float eps, uint32_t mode) {
+  Error err;
+  if (!check_iters(iters, &err) || !validate_mode(mode, &err)) return fail(err);
+  if (!std::isfinite(eps) || eps < 0.f) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (coeffs && !finite3(coeffs)) return fail(MUON_ERR_INVALID_ARG, "coefficients must be finite");
+  g_state.iters = iters;
+  if (coeffs) std::memcpy(g_state.coeffs, coeffs, sizeof g_state.coeffs);
+  g_state.eps = eps;
+  g_state.mode = mode;
+  return ok();
+}
+
+const char *muon_last_error(void) { return g_state.err.c_str(); }
+
+muon_status muon_set_phase_timing(int32_t enable) {
+  g_timing.on = enable != 0;
+  return ok();
+}
+
+muon_status muon_phase_times(double ms[6], int64_t launches[6]) {
+  double acc[kTKinds] = {};
+  int64_t cnt[kTKinds] = {};
+  for (size_t i = 0; i < g_timing.kinds.size(); ++i) {
+    hipError_t r = hipEventSynchronize(g_timing.pool[2 * i + 1]);
+    float t = 0.f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&t, g_timing.pool[2 * i], g_timing.pool[2 * i + 1]);
+    if (r != hipSuccess) {
+      g_timing.kinds.clear();
+      return hip_fail(r, "phase timing");
+    }
+    acc[g_timing.kinds[i]] += double(t);
+    cnt[g_timing.kinds[i]] += 1;
+  }
+  g_timing.kinds.clear();
+  for (int k = 0; k < kTKinds; ++k) {
+    if (ms) ms[k] = acc[k];
+    if (launches) launches[k] = cnt[k];
+  }
+  return ok();
+}
+
+muon_status muon_plan_info(const muon_mat *descs, int32_t n_mats, int32_t iters, uint32_t mode,
+                           size_t workspace_bytes, char *buf, size_t len, size_t *needed) {
+  Error err;
+  if (!validate_mode(mode, &err) || !check_iters(iters, &err) ||
+      !validate_descs(descs, n_mats, mode, "descs", &err))
+    return fail(err);
+  Plan plan;
+  if (!build_plan(descs, n_mats, iters, mode, workspace_bytes, &plan, &err)) return fail(err);
+  const std::string js = plan_json(plan);
+  if (needed) *needed = js.size() + 1;
+  if (buf && len) {
+    const size_t n = js.size() < len - 1 ? js.size() : len - 1;
+    std::memcpy(buf, js.data(), n);
+    buf[n] = 0;
+  }
+  return ok();
+}
+
+}  // extern "C"

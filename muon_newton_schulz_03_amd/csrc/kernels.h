@@ -1,0 +1,87 @@
+// Launch arguments shared by the host runtime and the HIP kernels.
+//
+// Workspace: every view (a whole matrix, or a column block in blockwise mode)
+// owns one block of the caller's workspace holding X and X^T (ping-pong), the
+// Gram matrix A (bf16 hi/lo halves, or float32), B = b A + c A A, the
+// per-tile partial sums of squares and its scale s = 1/(||X||_F + eps).
+// Views of one padded shape sit at a uniform stride ("segment"), so a grouped
+// launch needs only a handful of segment descriptors in its kernel arguments.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace muon {
+
+constexpr int kSegsMax = 8;
+constexpr int kElemViewsMax = 16;
+
+enum ElemKind : int32_t {
+  kPrepNs = 0,    // X0 = data
+  kPrepStep = 1,  // M <- beta M + G, X0 = M (or G + beta M)
+  kFinishNs = 2,  // data <- O
+  kFinishStep = 3 // W <- W - lr O
+};
+
+enum Phase : int32_t { kGram = 0, kAA = 1, kBX = 2 };
+
+struct ElemView {
+  const void *g;  // gradient view (prep step)
+  void *m;        // momentum view (step) or data view (ns)
+  void *w;        // weight view (finish step)
+  int64_t ld_g, ld_m, ld_w;  // elements
+  char *blk;                 // workspace block of the view
+  int64_t off_direct;        // buffer in the user's orientation (X if wide, X^T if tall)
+  int64_t off_trans;         // the other orientation (prep only)
+  int64_t off_part, off_scale;
+  int32_t rows, cols;        // view shape, user orientation
+  int32_t pitch_direct;      // row pitch (elements) of the direct buffer
+  int32_t pitch_trans;       // row pitch of the transposed buffer
+  int32_t tiles_c;           // 64-wide tiles along the user's columns
+  int32_t tile_begin;        // first tile of this view in the launch
+  int32_t vec;               // bit 0/1/2: g/m/w rows start on 16-byte boundaries
+  int32_t pad_;
+};
+
+struct ElemArgs {
+  ElemView v[kElemViewsMax];
+  int32_t nv;
+  int32_t total_tiles;
+  int32_t kind;
+  int32_t nesterov;
+  int32_t final_scale;  // finish: multiply O by s (iters == 0)
+  float beta, lr;
+};
+
+struct GemmSeg {
+  char *base;
+  int64_t stride;
+  int64_t off_xa[2], off_xt[2], off_ahi, off_alo, off_b, off_bdiag, off_part, off_scale;
+  int32_t mp, np;
+  int32_t count;
+  int32_t tiles_per_view;
+  int32_t tile_begin;
+  int32_t tn;      // tiles along n (B X phase)
+  int32_t nparts;  // partial sums per view
+  int32_t view_begin;
+};
+
+struct GemmArgs {
+  GemmSeg seg[kSegsMax];
+  int32_t nseg;
+  int32_t total_tiles;
+  int32_t src;      // X buffer read this iteration; the product goes to src ^ 1
+  int32_t first;    // first iteration: apply the normalization scale
+  int32_t aa_plain; // A*A from bf16(A) only
+  int32_t remap;    // XCD-aware tile order
+  float a, b, c;
+  float eps;
+};
+
+// Launchers (kernels.hip). Each returns the HIP error of the launch.
+hipError_t launch_elem(const ElemArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_norm_finalize(const GemmArgs &a, int views, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs &a, int phase, bool bf16, hipStream_t s);
+
+}  // namespace muon

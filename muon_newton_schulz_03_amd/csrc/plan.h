@@ -1,0 +1,122 @@
+// Host-side validation and scheduling for the Muon library. Plain C++ with no
+// HIP dependency, so it builds and runs on a machine without a GPU.
+//
+// The unit of work is a "view": one whole matrix, or one column block of it
+// in blockwise mode. A view of rows x cols is oriented wide (m = min, n = max;
+// transposed when rows > cols) and padded to (mp, np), multiples of the
+// kernel tile. Zero padding is exact for the iteration: padded rows and
+// columns of X stay zero through A = X X^T, B = b A + c A A and a X + B X.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+
+namespace muon {
+
+constexpr int kMaxSegs = 8;          // uniform-shape segments per grouped launch
+constexpr int kMaxElemViews = 16;    // views per element-wise launch
+constexpr int64_t kMaxMinDim = 32768;
+constexpr int64_t kMaxMaxDim = 4194304;
+constexpr int kMaxIters = 64;
+constexpr int32_t kMaxMats = 1 << 20;
+constexpr int kPadBf16 = 256;        // bf16 matrix-core tile
+constexpr int kPadF32 = 64;          // float32 tile
+constexpr int kElemTile = 64;        // element-wise kernels work on 64x64 tiles
+constexpr int kGemmTile = 256;
+
+// Byte offsets of the buffers of one view inside its workspace block.
+struct Layout {
+  size_t xa[2];     // X, mp x np row-major (ping-pong)
+  size_t xt[2];     // X^T, np x mp row-major (ping-pong)
+  size_t ahi, alo;  // A = X X^T (bf16 hi/lo halves; float32 path uses ahi only)
+  size_t b;         // B = b A + c A A (bf16 path: diagonal stored as zero)
+  size_t bdiag;     // bf16 path: diagonal of B in float32
+  size_t partials;  // per-64x64-tile sums of squares (float)
+  size_t scale;     // s = 1/(||X||_F + eps), s^2 (float)
+  size_t total;
+  int64_t nparts;
+};
+
+Layout view_layout(int64_t mp, int64_t np, bool bf16);
+
+struct View {
+  int32_t mat = 0, block = 0;
+  int64_t rows = 0, cols = 0;  // user orientation
+  int64_t col_off = 0;         // first column of the block inside the matrix
+  bool tall = false;
+  int64_t m = 0, n = 0;        // wide
+  int64_t mp = 0, np = 0;      // padded wide
+  double cost = 0;             // nominal flops iters * (4 m^2 n + 2 m^3)
+  size_t bytes = 0;            // workspace block size
+};
+
+struct Segment {
+  int32_t first = 0, count = 0;  // views [first, first+count) of the plan order
+  int64_t mp = 0, np = 0;
+  size_t base = 0;               // workspace offset of the first view's block
+  size_t stride = 0;             // bytes between consecutive blocks
+  int64_t tiles_syrk = 0, tiles_gemm = 0, tiles_elem = 0;  // per view
+};
+
+struct Chunk {
+  int32_t first = 0, count = 0;
+  std::vector<Segment> segs;
+  size_t bytes = 0;
+};
+
+struct Plan {
+  bool bf16 = true;
+  int pad = kPadBf16;
+  int iters = 5;
+  uint32_t mode = 0;
+  std::vector<View> views;  // processing order
+  std::vector<Chunk> chunks;
+  size_t full_bytes = 0, min_bytes = 0;
+};
+
+struct Error {
+  muon_status status = MUON_OK;
+  std::string msg;
+  bool set(muon_status s, const std::string &m) {
+    status = s;
+    msg = m;
+    return false;
+  }
+};
+
+size_t dtype_size(int32_t dtype);
+
+// Checks one descriptor array (shapes, dtype, alignment, blocks).
+bool validate_descs(const muon_mat *d, int32_t n, uint32_t mode, const char *what, Error *err);
+// muon_step: params/grads/moms agree per matrix.
+bool validate_step_triplets(const muon_mat *w, const muon_mat *g, const muon_mat *m, int32_t n,
+                            Error *err);
+// Written buffers must not overlap any other buffer of the call. `writable`
+// flags which of the arrays are written.
+bool check_alias(const muon_mat *const *arrays, const bool *writable, int narrays, int32_t n,
+                 Error *err);
+bool validate_mode(uint32_t mode, Error *err);
+
+// Orders the views, groups them into chunks that fit `ws_bytes` (0 = as
+// many as needed to hold everything at once) and into uniform segments.
+bool build_plan(const muon_mat *d, int32_t n, int32_t iters, uint32_t mode, size_t ws_bytes,
+                Plan *plan, Error *err);
+
+std::string plan_json(const Plan &p);
+
+// Exact element-overlap test of two strided matrices (byte addresses).
+bool matrices_overlap(const muon_mat &a, const muon_mat &b);
+
+// Upper-triangle tile index u -> (I, J), I <= J, enumerated column by column.
+inline void syrk_tile(int64_t u, int64_t *I, int64_t *J) {
+  int64_t j = 0;
+  while ((j + 1) * (j + 2) / 2 <= u) ++j;
+  *J = j;
+  *I = u - j * (j + 1) / 2;
+}
+
+}  // namespace muon

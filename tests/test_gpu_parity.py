@@ -1,0 +1,231 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Small and ragged shapes that span several tiles and leave ragged tails, both
+precision paths, every mode bit, and the edge cases (zero iterations, zero
+matrix, NaN input, empty batch, single row/column). Tolerances: relative
+Frobenius error <= 1e-4 on the float32 path and <= 2e-2 on the bf16 path
+(per matrix, against the float64 oracle on the same stored inputs); the
+element-wise kernels within 1 bf16 ulp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import bf16_round, bf16_ulp_diff, np64, padded, relF
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+def rand(shape, dtype, seed, std=1.0, ld=None):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    base, view = padded(shape[0], shape[1], dtype, ld)
+    view.copy_(torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std)
+    return base, view
+
+
+# ---------------------------------------------------------------------------
+# float32 path
+# ---------------------------------------------------------------------------
+
+def test_f32_step_64x128(gpu_lib):
+    from muon_newton_schulz_03_amd.workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS["fp32_64x128"]
+    W, G, M = make_inputs(wl)
+    W0, G0, M0 = np64(W[0]), np64(G[0]), np64(M[0])
+    gpu_lib.muon_step(W, G, M, lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov, iters=wl.iters)
+    torch.cuda.synchronize()
+    O_ref, M_ref, W_ref = oracle.muon_step(W0, G0, M0, lr=wl.lr, beta=wl.beta)
+    assert relF(np64(M[0]), M_ref) <= F32_TOL
+    assert relF(W0 - np64(W[0]), W0 - W_ref) <= F32_TOL
+
+
+@pytest.mark.parametrize("shape,ld", [((100, 37), 40), ((37, 100), 103), ((1, 50), 50), ((64, 64), 64),
+                                      ((130, 260), 264), ((300, 7), 7), ((65, 65), 66)])
+def test_f32_ns_ragged(gpu_lib, shape, ld):
+    base, X = rand(shape, torch.float32, 7, ld=ld)
+    X0 = np64(X)
+    gpu_lib.muon_ns_batched([X], iters=5)
+    torch.cuda.synchronize()
+    assert relF(np64(X), oracle.newton_schulz(X0)) <= F32_TOL
+    if ld > shape[1]:
+        assert torch.isnan(base[:, shape[1]:]).all()  # pitch padding untouched
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3])
+def test_f32_iters(gpu_lib, iters):
+    _, X = rand((40, 90), torch.float32, 3)
+    X0 = np64(X)
+    gpu_lib.muon_ns_batched([X], iters=iters)
+    torch.cuda.synchronize()
+    assert relF(np64(X), oracle.newton_schulz(X0, iters=iters)) <= F32_TOL
+
+
+# ---------------------------------------------------------------------------
+# bf16 path
+# ---------------------------------------------------------------------------
+
+BF16_SHAPES = [((300, 520), 520), ((520, 300), 304), ((256, 256), 256), ((1, 64), 64), ((64, 1), 8),
+               ((1, 96), 96), ((2, 300), 304),
+               ((777, 1030), 1032), ((512, 2048), 2048), ((1030, 777), 777)]
+
+
+@pytest.mark.parametrize("shape,ld", BF16_SHAPES)
+def test_bf16_ns_ragged(gpu_lib, shape, ld):
+    base, X = rand(shape, torch.bfloat16, 11, std=0.01, ld=ld)
+    X0 = np64(X)
+    gpu_lib.muon_ns_batched([X], iters=5)
+    torch.cuda.synchronize()
+    err = relF(np64(X), oracle.newton_schulz(X0))
+    print(f"shape {shape} relF {err:.3e}")
+    assert err <= BF16_TOL
+    if ld > shape[1]:
+        assert torch.isnan(base[:, shape[1]:].float()).all()
+
+
+@pytest.mark.parametrize("nesterov", [False, True])
+def test_bf16_step_batch(gpu_lib, nesterov):
+    shapes = [(300, 520), (520, 300), (256, 768), (64, 64), (1, 96)]
+    G = [rand(s, torch.bfloat16, 100 + i, std=1e-3)[1] for i, s in enumerate(shapes)]
+    M = [rand(s, torch.bfloat16, 200 + i, std=1e-2)[1] for i, s in enumerate(shapes)]
+    W = [rand(s, torch.bfloat16, 300 + i, std=0.02)[1] for i, s in enumerate(shapes)]
+    G0, M0, W0 = [np64(t) for t in G], [np64(t) for t in M], [np64(t) for t in W]
+    # the ABI takes lr and beta as float32; the oracle gets those same values
+    lr, beta = float(np.float32(0.02)), float(np.float32(0.95))
+    # run 1: W = 0 and lr = -1 make W_new = O exactly (O is bf16 already)
+    Wz = [torch.zeros_like(t) for t in W]
+    Mc = [t.clone() for t in M]
+    gpu_lib.muon_step(Wz, G, Mc, lr=-1.0, beta=beta, nesterov=nesterov)
+    torch.cuda.synchronize()
+    O_gpu = [np64(t) for t in Wz]
+    for i in range(len(shapes)):
+        O_ref, M_ref, _ = oracle.muon_step(W0[i], G0[i], M0[i], lr=lr, beta=beta, nesterov=nesterov)
+        err = relF(O_gpu[i], O_ref)
+        print(f"{shapes[i]} O relF {err:.3e}")
+        assert err <= BF16_TOL
+        assert bf16_ulp_diff(np64(Mc[i]), bf16_round(M_ref)).max() <= 1
+    # run 2: real weights; the update is pinned given the O of run 1
+    Mc2 = [t.clone() for t in M]
+    gpu_lib.muon_step(W, G, Mc2, lr=lr, beta=beta, nesterov=nesterov)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(Mc2[i], Mc[i])
+        expect = bf16_round(W0[i] - lr * O_gpu[i])
+        assert bf16_ulp_diff(np64(W[i]), expect).max() <= 1
+
+
+@pytest.mark.parametrize("shape,k", [((512, 1536), 3), ((1024, 768), 4), ((300, 520), 2)])
+def test_bf16_blockwise(gpu_lib, shape, k):
+    import muon_newton_schulz_03_amd as mu
+    _, X = rand(shape, torch.bfloat16, 21, std=0.01)
+    X0 = np64(X)
+    Y = X.clone()
+    gpu_lib.muon_ns_batched([X], iters=5, mode=mu.MUON_NS_BLOCKWISE | mu.MUON_PACK_COST, col_blocks=k)
+    # the same blocks as separate (strided) matrices in one call
+    w = shape[1] // k
+    gpu_lib.muon_ns_batched([Y[:, j * w:(j + 1) * w] for j in range(k)], iters=5)
+    torch.cuda.synchronize()
+    assert torch.equal(X, Y)
+    ref = oracle.newton_schulz_blockwise(X0, k)
+    for j in range(k):
+        assert relF(np64(X[:, j * w:(j + 1) * w]), ref[:, j * w:(j + 1) * w]) <= BF16_TOL
+    assert relF(np64(X), oracle.newton_schulz(X0)) > 5e-2  # not the whole-matrix result
+
+
+def test_bf16_symmetric_intermediates(gpu_lib):
+    """After one iteration the workspace holds A (hi, lo) and B of it: both
+    bitwise symmetric (mirrored), A equal to s^2 X0 X0^T, zero padding."""
+    import muon_newton_schulz_03_amd as mu
+    shape = (300, 520)
+    _, X = rand(shape, torch.bfloat16, 5, std=0.01)
+    X0 = np64(X)
+    gpu_lib.muon_ns_batched([X], iters=1, mode=mu.MUON_PACK_RR)
+    torch.cuda.synchronize()
+    plan = mu.muon_plan_info([mu.mat_of(X)], iters=1, mode=mu.MUON_PACK_RR,
+                             workspace_bytes=mu._ws.nbytes)
+    seg = plan["chunks"][0]["segments"][0]
+    L = seg["layout"]
+    mp = seg["mp"]
+    buf = mu._ws.buf
+
+    def mat(off):
+        return buf[seg["base"] + off: seg["base"] + off + mp * mp * 2].view(torch.bfloat16).view(mp, mp)
+    Ah, Al, B = mat(L["ahi"]), mat(L["alo"]), mat(L["b"])
+    for T in (Ah, Al, B):
+        assert torch.equal(T, T.t())
+    A = np64(Ah) + np64(Al)
+    s = 1.0 / (np.linalg.norm(X0) + 1e-7)
+    m = shape[0]
+    assert relF(A[:m, :m], s * s * (X0 @ X0.T)) < 1e-4
+    assert np.all(A[m:, :] == 0) and np.all(A[:, m:] == 0)
+    # B is stored with a zero diagonal; its diagonal is kept in float32
+    assert torch.all(torch.diagonal(B) == 0)
+    off = seg["base"] + L["bdiag"]
+    bdiag = buf[off: off + mp * 4].view(torch.float32).cpu().numpy().astype(np.float64)
+    Bfull = np64(B) + np.diag(bdiag)
+    Bref = -4.7750 * A + 2.0315 * (A @ A)
+    assert relF(Bfull, Bref) < 1e-2
+    assert np.allclose(bdiag, np.diag(Bref), rtol=1e-4, atol=1e-7)
+
+
+def test_bf16_deterministic_and_packing_invariant(gpu_lib):
+    import muon_newton_schulz_03_amd as mu
+    shapes = [(256, 768), (520, 300), (512, 1024), (300, 520), (256, 768)]
+    src = [rand(s, torch.bfloat16, 40 + i, std=0.01)[1] for i, s in enumerate(shapes)]
+    outs = []
+    for mode, cap in [(mu.MUON_PACK_COST, None), (mu.MUON_PACK_COST, None), (mu.MUON_PACK_RR, None),
+                      (mu.MUON_PACK_RR, 1)]:
+        xs = [t.clone() for t in src]
+        if cap is not None:  # a workspace of one matrix: one group per matrix
+            mu._ws = None
+            cap = mu.muon_workspace_min_size([mu.mat_of(t) for t in xs], mode)
+        gpu_lib.muon_ns_batched(xs, iters=5, mode=mode, max_workspace_bytes=cap)
+        torch.cuda.synchronize()
+        outs.append(xs)
+        mu._ws = None
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, BF16_TOL), (torch.float32, F32_TOL)])
+def test_iters_zero_normalizes(gpu_lib, dtype, tol):
+    _, X = rand((300, 520), dtype, 8, std=0.3)
+    X0 = np64(X)
+    gpu_lib.muon_ns_batched([X], iters=0)
+    torch.cuda.synchronize()
+    assert relF(np64(X), oracle.newton_schulz(X0, iters=0)) <= (5e-3 if dtype == torch.bfloat16 else tol)
+
+
+def test_zero_and_nan_matrices(gpu_lib):
+    Z = torch.zeros((130, 300), dtype=torch.bfloat16, device="cuda")
+    _, N = rand((130, 300), torch.bfloat16, 9, std=0.01)
+    N[5, 7] = float("nan")
+    _, X = rand((130, 300), torch.bfloat16, 10, std=0.01)
+    X0 = np64(X)
+    gpu_lib.muon_ns_batched([Z, N, X], iters=5)
+    torch.cuda.synchronize()
+    assert torch.all(Z == 0)
+    assert torch.isnan(N.float()).all()       # the norm is NaN, so every entry is
+    assert torch.isfinite(X.float()).all()    # neighbours in the batch are unaffected
+    assert relF(np64(X), oracle.newton_schulz(X0)) <= BF16_TOL
+
+
+def test_empty_batch(gpu_lib):
+    gpu_lib.muon_ns_batched([], iters=5)
+    gpu_lib.muon_step([], [], [], lr=0.02, beta=0.95)
+
+
+def test_aa_plain_mode(gpu_lib):
+    import muon_newton_schulz_03_amd as mu
+    _, X = rand((512, 2048), torch.bfloat16, 12, std=0.01)
+    X0 = np64(X)
+    gpu_lib.muon_ns_batched([X], iters=5, mode=mu.MUON_AA_PLAIN)
+    torch.cuda.synchronize()
+    err = relF(np64(X), oracle.newton_schulz(X0))
+    print(f"plain A*A relF {err:.3e}")
+    assert err < 6e-2

@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the CPU-oracle sample (0 disables it)")
     p.add_argument("--no-phase-timing", action="store_true")
+    p.add_argument("--matrices", type=int, default=0,
+                   help="use only the first N matrices of the workload (diagnostics; 0 = all)")
     return p.parse_args()
 
 
@@ -104,6 +106,9 @@ def main():
 
     mu.load_library()
     wl = WORKLOADS[args.workload]
+    if args.matrices:
+        import dataclasses
+        wl = dataclasses.replace(wl, name=f"{wl.name}[:{args.matrices}]", shapes=wl.shapes[:args.matrices])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     mode = (mu.MUON_PACK_COST if args.pack == "cost" else mu.MUON_PACK_RR)

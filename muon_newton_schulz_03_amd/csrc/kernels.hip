@@ -38,6 +38,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // tile bookkeeping
@@ -232,12 +233,20 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const GemmArgs args)
 }
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core kernel: 256x256 output tile, K step 64, 4 waves (2x2),
-// each wave 128x128 = 4x4 blocks of v_mfma_f32_32x32x16_bf16.
-// Operand tiles (256 rows x 64 k, bf16) are staged through LDS, double
-// buffered (2 stages x 2 operands x 32 KiB); each 128-byte row keeps its
-// eight 16-byte chunks XOR-swizzled by (row & 7) so that the fragment reads
-// (32 rows, one chunk each) spread over the banks.
+// bf16 matrix-core kernel: 256x256 output tile, 4 waves (2x2), each wave
+// 128x128 = 4x4 blocks of v_mfma_f32_32x32x16_bf16.
+//
+// Operands stream through a 4-stage LDS ring (stage = 256 rows x 32 k of
+// both operands, 2 x 16 KiB). Global memory goes straight to LDS with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at LDS base + 16 * lane),
+// issued three K steps ahead, so no registers hold staged data and the load
+// latency hides behind three steps of matrix work. One barrier per K step:
+// after it, step ks + 1 is visible to every wave and the stage of step
+// ks - 1 is free for the loads of step ks + 3.
+//
+// A 64-byte LDS row holds four 16-byte chunks of k, XOR-swizzled by
+// ((row >> 2) & 3): the 16 lanes of a fragment-read group (16 consecutive
+// rows, one logical chunk) then hit 16 distinct 4-bank groups of the 64 banks.
 //
 // MFMA 32x32x16 register layout: lane l supplies row (l & 31) of the A
 // operand and column (l & 31) of the B operand, each as 8 consecutive k
@@ -246,105 +255,155 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const GemmArgs args)
 // C[8 (r >> 2) + 4 (l >> 5) + (r & 3)][l & 31].
 // ---------------------------------------------------------------------------
 
-constexpr int kBM = 256, kBK = 64;
-constexpr int kOpBytes = kBM * kBK * 2;  // one operand tile, one stage
+constexpr int kBM = 256, kBK = 32, kStages = 4;
+constexpr int kOpBytes = kBM * kBK * 2;          // one operand tile, one stage (16 KiB)
+constexpr int kStageBytes = 2 * kOpBytes;        // both operands
 
-// Epilogue of one 32x32 accumulator block: rows ib + 8 r4 + q (q = 0..3),
-// column j, for r4 = 0..3 (see the MFMA layout above).
-template <int PHASE>
-struct GemmEpilogue {
-  int mp, np, ib, jb;
-  bool diag;
-  float a, b, c, scale;
-  bf16 *ahi, *alo, *bm, *ya, *yt;
-  const bf16 *xt;
-  float *bdiag;
+// ---------------------------------------------------------------------------
+// Epilogues. After the K loop the LDS ring (128 KiB) holds one 256 x 256 bf16
+// tile: 512-byte rows whose 16-byte chunks are XOR-swizzled by
+// row ^ ((row & 3) << 2) (mod 32), which spreads both 32 consecutive rows at
+// one column and 4 consecutive rows at 8 consecutive columns over the banks.
+// Accumulators go to that tile in whichever orientation a pass needs, and the
+// tile then leaves as coalesced 16-byte row stores (and arrives the same way
+// when an epilogue needs a tile of another matrix).
+// ---------------------------------------------------------------------------
 
-  __device__ inline void block(const f32x16 &acc, int i0, int j) const {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int i = i0 + r4 * 8;  // rows i .. i+3, column j
-      if (PHASE == kBX) {
-        // X' = s'' (a X + B X); X[i..i+3][j] = X^T[j][i..i+3]
-        // B's diagonal is kept in float32 (bdiag) and is zero in the bf16 B
-        // operand, so the diagonal part of B X is (a + B_ii) X[i][j] here
-        const bf16x4 x4 = *reinterpret_cast<const bf16x4 *>(xt + int64_t(j) * mp + i);
-        const float4 d4 = *reinterpret_cast<const float4 *>(bdiag + i);
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-        bf16x4 o4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o4[q] = bf16(scale * fmaf(a + dd[q], float(x4[q]), acc[r4 * 4 + q]));
-        *reinterpret_cast<bf16x4 *>(yt + int64_t(j) * mp + i) = o4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ya[int64_t(i + q) * np + j] = o4[q];
-        continue;
-      }
-      bf16x4 v1, v2;
-      if (PHASE == kGram) {
-        // A = s' X X^T, kept as bf16 hi + lo
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v = acc[r4 * 4 + q] * scale;
-          v1[q] = bf16(v);
-          v2[q] = bf16(v - float(v1[q]));
-        }
-      } else {
-        // B = b A + c A A; A[i..i+3][j] = A[j][i..i+3] (A is symmetric).
-        // The diagonal goes to bdiag in float32 and is stored as zero in B.
-        const bf16x4 h4 = *reinterpret_cast<const bf16x4 *>(ahi + int64_t(j) * mp + i);
-        const bf16x4 l4 = *reinterpret_cast<const bf16x4 *>(alo + int64_t(j) * mp + i);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float bv = fmaf(b, float(h4[q]) + float(l4[q]), c * acc[r4 * 4 + q]);
-          v1[q] = bf16(bv);
-          if (diag && i + q == j) {
-            bdiag[j] = bv;
-            v1[q] = bf16(0.f);
-          }
-        }
-      }
-      bf16 *o1 = PHASE == kGram ? ahi : bm;
-      bf16 *o2 = alo;
-      if (!diag) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o1[int64_t(i + q) * mp + j] = v1[q];
-          if (PHASE == kGram) o2[int64_t(i + q) * mp + j] = v2[q];
-        }
-        *reinterpret_cast<bf16x4 *>(o1 + int64_t(j) * mp + i) = v1;
-        if (PHASE == kGram) *reinterpret_cast<bf16x4 *>(o2 + int64_t(j) * mp + i) = v2;
-      } else {
-        // diagonal tile: keep the upper element and mirror it, so the stored
-        // matrix is symmetric bit for bit
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ii = i + q;
-          if (ii <= j) {
-            o1[int64_t(ii) * mp + j] = v1[q];
-            if (PHASE == kGram) o2[int64_t(ii) * mp + j] = v2[q];
-          }
-          if (ii < j) {
-            o1[int64_t(j) * mp + ii] = v1[q];
-            if (PHASE == kGram) o2[int64_t(j) * mp + ii] = v2[q];
-          }
-        }
-      }
-    }
+__device__ inline int tile_chunk(int row, int c) { return (c ^ row ^ ((row & 3) << 2)) & 31; }
+__device__ inline int tile_off(int row, int col) {
+  return row * 512 + (tile_chunk(row, col >> 3) << 4) + (col & 7) * 2;
+}
+
+// Calls f(acc[bi][bj], bi, bj) for the 16 accumulator blocks with
+// compile-time indices, so the accumulators stay in registers.
+template <class F, int... N>
+__device__ inline void for_blocks(f32x16 (&acc)[4][4], F &&f, std::integer_sequence<int, N...>) {
+  (f(acc[N / 4][N % 4], N / 4, N % 4), ...);
+}
+template <class F>
+__device__ inline void for_blocks(f32x16 (&acc)[4][4], F &&f) {
+  for_blocks(acc, f, std::make_integer_sequence<int, 16>{});
+}
+
+// tile (256 x 256 at row0, col0 of a row-major matrix with `pitch`) <-> LDS
+__device__ inline void tile_store(const char *smem, bf16 *dst, int64_t pitch, int row0, int col0, int tid) {
+#pragma unroll 8
+  for (int k = 0; k < 32; ++k) {
+    const int u = tid + 256 * k, row = u >> 5, c = u & 31;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + row * 512 + (tile_chunk(row, c) << 4));
+    *reinterpret_cast<u32x4 *>(dst + int64_t(row0 + row) * pitch + col0 + c * 8) = v;
   }
+}
+__device__ inline void tile_load(char *smem, const bf16 *src, int64_t pitch, int row0, int col0, int tid) {
+#pragma unroll 8
+  for (int k = 0; k < 32; ++k) {
+    const int u = tid + 256 * k, row = u >> 5, c = u & 31;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + int64_t(row0 + row) * pitch + col0 + c * 8);
+    *reinterpret_cast<u32x4 *>(smem + row * 512 + (tile_chunk(row, c) << 4)) = v;
+  }
+}
+
+// Barrier for LDS hand-offs inside the epilogue: waits for this wave's LDS
+// operations only, not for its global stores (a full __syncthreads() fence
+// would wait for every store of the previous pass to land).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+}
+
+// Diagonal tile: the LDS tile holds L[c][r] = value computed at (r, c).
+// Output row r takes element c from the upper-triangle computation
+// (min(r, c), max(r, c)), so the stored tile is symmetric bit for bit.
+__device__ inline void tile_store_sym(const char *smem, bf16 *dst, int64_t pitch, int row0, int col0, int tid) {
+  bf16 *d = dst + int64_t(row0 + tid) * pitch + col0;
+  const int r = tid;
+#pragma unroll 4
+  for (int cc = 0; cc < 32; ++cc) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = 8 * cc + e;
+      v[e] = *reinterpret_cast<const bf16 *>(smem + (c >= r ? tile_off(c, r) : tile_off(r, c)));
+    }
+    *reinterpret_cast<bf16x8 *>(d + 8 * cc) = v;
+  }
+}
+
+// Accumulator element (r4 * 4 + q) of block (bi, bj) sits at tile row
+// ti = wm*128 + bi*32 + r4*8 + fh*4 + q and tile column tj = wn*128 + bj*32 + fr.
+struct EpiCoord {
+  int ib, jb;  // wm*128 + fh*4, wn*128 + fr
 };
 
-// Applies the epilogue to the 16 accumulator blocks with compile-time
-// indices, so the accumulators stay in registers.
-template <int PHASE, int... N>
-__device__ inline void run_epilogue(const f32x16 (&acc)[4][4], const GemmEpilogue<PHASE> &ep,
-                                    std::integer_sequence<int, N...>) {
-  (ep.block(acc[N / 4][N % 4], ep.ib + (N / 4) * 32, ep.jb + (N % 4) * 32), ...);
+// Accumulators converted once and kept bit-packed in place: the bf16 bit
+// pattern sits in bits [shift, shift + 16) of each 32-bit register. Vector
+// elements are reinterpreted with __float_as_uint / __uint_as_float:
+// __builtin_bit_cast on a vector-element operand reads element 0.
+__device__ inline uint32_t pack_bf16(float hi, float lo) {
+  const bf16 h = bf16(hi), l = bf16(lo);
+  return (uint32_t(__builtin_bit_cast(uint16_t, h)) << 16) | uint32_t(__builtin_bit_cast(uint16_t, l));
+}
+// the four bf16 of rows r4*4 .. r4*4+3 as two 32-bit words (element q in
+// bits 16 (q & 1) of word q >> 1), built with integer operations only
+__device__ inline u32x2 unpack4(const f32x16 &a, int r4, int shift) {
+  uint32_t x[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) x[q] = (__float_as_uint(a[r4 * 4 + q]) >> shift) & 0xFFFFu;
+  return u32x2{x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
+}
+// writes block (bi, bj) of the packed accumulators into the LDS tile,
+// transposed ([tj][ti], 8-byte writes) or direct ([ti][tj], 2-byte writes)
+template <bool TRANS>
+__device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const struct EpiCoord &e, int shift);
+
+// [ti][tj] orientation. Within each quad of lanes (4 consecutive columns)
+// the 4 x 4 block of bf16 (4 rows x 4 columns) is transposed with two DPP
+// quad permutes, after which lane p of the quad holds row p of the block as
+// 4 consecutive columns: one 8-byte write.
+__device__ inline uint32_t quad_xor2(uint32_t v) { return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)); }
+__device__ inline uint32_t quad_xor1(uint32_t v) { return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)); }
+__device__ inline u32x2 quad_transpose(u32x2 w, int p) {
+  const bool hi2 = p & 2, odd = p & 1;
+  const uint32_t y = quad_xor2(hi2 ? w[0] : w[1]);
+  const uint32_t x0 = hi2 ? y : w[0], x1 = hi2 ? w[1] : y;
+  const uint32_t z0 = quad_xor1(x0), z1 = quad_xor1(x1);
+  return odd ? u32x2{(z0 >> 16) | (x0 & 0xFFFF0000u), (z1 >> 16) | (x1 & 0xFFFF0000u)}
+             : u32x2{(x0 & 0xFFFFu) | (z0 << 16), (x1 & 0xFFFFu) | (z1 << 16)};
+}
+__device__ inline void put_direct(char *smem, const EpiCoord &e, int bi, int bj, int r4, u32x2 v) {
+  const int p = e.jb & 3;
+  const u32x2 t = quad_transpose(v, p);
+  const int ti = e.ib + bi * 32 + r4 * 8 + p, tj = e.jb - p + bj * 32;
+  *reinterpret_cast<u32x2 *>(smem + tile_off(ti, tj)) = t;
+}
+// [tj][ti .. ti+3] orientation: one 8-byte write
+__device__ inline void put_trans(char *smem, const EpiCoord &e, int bi, int bj, int r4, u32x2 v) {
+  const int tj = e.jb + bj * 32, ti = e.ib + bi * 32 + r4 * 8;
+  *reinterpret_cast<u32x2 *>(smem + tile_off(tj, ti)) = v;
+}
+__device__ inline bf16x4 get_trans(const char *smem, const EpiCoord &e, int bi, int bj, int r4) {
+  const int tj = e.jb + bj * 32, ti = e.ib + bi * 32 + r4 * 8;
+  return *reinterpret_cast<const bf16x4 *>(smem + tile_off(tj, ti));
+}
+
+template <bool TRANS>
+__device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const EpiCoord &e, int shift) {
+  for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const u32x2 v = unpack4(a, r4, shift);
+      if (TRANS)
+        put_trans(smem, e, bi, bj, r4, v);
+      else
+        put_direct(smem, e, bi, bj, r4, v);
+    }
+  });
 }
 
 template <int PHASE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const GemmArgs args) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kOpBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
@@ -374,13 +433,21 @@ void gemm_bf16_kernel(const GemmArgs args) {
     K = mp;
   }
 
-  // global -> register -> LDS staging: thread t moves 16-byte chunk (t & 7)
-  // of rows (t >> 3) + 32 q, q = 0..7, of both operand tiles.
-  const int lrow = tid >> 3, lkc = tid & 7;
-  const int64_t prow = int64_t(i0 + lrow) * ld + lkc * 8;
-  const int64_t qrow = int64_t(j0 + lrow) * ld + lkc * 8;
-  const int sw_off = lrow * 128 + ((lkc ^ (lrow & 7)) << 4);
-  u32x4 ra[8], rb[8];
+  // Global -> LDS: each wave issues 4 loads per operand per K step; load q of
+  // wave w fills rows (4 w + q) * 16 .. + 15 (1 KiB). Lane L carries row
+  // base + L / 4 and the logical k chunk that belongs in physical chunk L % 4.
+  const int lrow0 = lane >> 2;
+  const int lphys = lane & 3;
+  int64_t goff[4];   // element offset of this lane's 16 bytes, per q (k0 = 0)
+  int loff[4];       // LDS byte offset of the 1 KiB block, per q (wave-uniform)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = (wv * 4 + q) * 16 + lrow0;
+    const int lc = lphys ^ ((row >> 2) & 3);
+    goff[q] = int64_t(row) * ld + lc * 8;
+    loff[q] = (wv * 4 + q) * 1024;
+  }
+  const int64_t prow0 = int64_t(i0) * ld, qrow0 = int64_t(j0) * ld;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -390,83 +457,215 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
-  const int fr = lane & 31, fh = lane >> 5, fx = lane & 7;
+  const int fr = lane & 31, fh = lane >> 5;
   const int nk = K / kBK;
-  for (int ks = -1; ks < nk; ++ks) {
-    // prefetch K step ks + 1 into registers (for AA: K runs over three
-    // segments of length mp -- hi*hi, hi*lo, lo*hi)
-    if (ks + 1 < nk) {
-      int k0 = (ks + 1) * kBK;
-      const bf16 *pa = P, *qa = Q;
-      if (PHASE == kAA) {
-        const int sgm = k0 / mp;
-        k0 -= sgm * mp;
-        if (sgm == 2) pa = P2;
-        if (sgm == 1) qa = Q2;
-      }
+  // byte offset of this lane's fragment rows inside an operand tile; the
+  // swizzle term (row >> 2) & 3 depends on the lane only (block bases are
+  // multiples of 32 rows)
+  const int fa = (wm * 128 + fr) * 64, fb = (wn * 128 + fr) * 64;
+  const int fx = (fr >> 2) & 3;
+
+  // issue the loads of K step ks_ into its stage (for A*A, K runs over three
+  // segments of length mp: hi*hi, hi*lo, lo*hi)
+#define MUON_GLOAD(ks_)                                                              \
+  do {                                                                               \
+    int k0_ = (ks_) * kBK;                                                           \
+    const bf16 *pa_ = P, *qa_ = Q;                                                   \
+    if (PHASE == kAA) {                                                              \
+      const int sgm_ = k0_ / mp;                                                     \
+      k0_ -= sgm_ * mp;                                                              \
+      pa_ = sgm_ == 2 ? P2 : P;                                                      \
+      qa_ = sgm_ == 1 ? Q2 : Q;                                                      \
+    }                                                                                \
+    char *st_ = smem + ((ks_) & (kStages - 1)) * kStageBytes;                        \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
+      __builtin_amdgcn_global_load_lds(                                              \
+          (const __attribute__((address_space(1))) void *)(pa_ + prow0 + goff[q] + k0_), \
+          (__attribute__((address_space(3))) void *)(st_ + loff[q]), 16, 0, 0);      \
+      __builtin_amdgcn_global_load_lds(                                              \
+          (const __attribute__((address_space(1))) void *)(qa_ + qrow0 + goff[q] + k0_), \
+          (__attribute__((address_space(3))) void *)(st_ + kOpBytes + loff[q]), 16, 0, 0); \
+    }                                                                                \
+  } while (0)
+#define MUON_FRAGS(buf_, ks_, kk_)                                                   \
+  do {                                                                               \
+    const char *As_ = smem + ((ks_) & (kStages - 1)) * kStageBytes;                  \
+    const char *Bs_ = As_ + kOpBytes;                                                \
+    const int ch_ = (((kk_) * 2 + fh) ^ fx) << 4;                                    \
+    _Pragma("unroll") for (int bi = 0; bi < 4; ++bi)                                 \
+      af[buf_][bi] = *reinterpret_cast<const bf16x8 *>(As_ + fa + bi * 2048 + ch_);  \
+    _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                                 \
+      bq[buf_][bj] = *reinterpret_cast<const bf16x8 *>(Bs_ + fb + bj * 2048 + ch_);  \
+  } while (0)
+#define MUON_MFMA(buf_)                                                              \
+  do {                                                                               \
+    _Pragma("unroll") for (int bi = 0; bi < 4; ++bi)                                 \
+      _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                               \
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf_][bi], bq[buf_][bj], acc[bi][bj], 0, 0, 0); \
+  } while (0)
+  // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+  // [15:14], expcnt[6:4] and lgkmcnt[11:8] left at their maxima)
+#define MUON_WAIT_VM(n_) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0F70)
+
+  // Steps past the end re-load the last step into a stage nobody reads
+  // again; this keeps 8 loads per wave per step, so the vmcnt arithmetic
+  // below is the same in every iteration.
+  const int kl = nk - 1;
+  bf16x8 af[2][4], bq[2][4];
+  MUON_GLOAD(0);
+  MUON_GLOAD(1 < kl ? 1 : kl);
+  MUON_GLOAD(2 < kl ? 2 : kl);
+  MUON_WAIT_VM(16);  // step 0 landed (steps 1, 2 in flight)
+  __syncthreads();
+  MUON_FRAGS(0, 0, 0);
+  for (int ks = 0; ks < nk; ++ks) {
+    // Step ks + 1 landed for this wave (ks + 2 in flight); after the barrier
+    // it has landed for every wave, and every wave has consumed step ks - 1.
+    // A bare s_barrier: the fragment reads still in flight here target step
+    // ks (stage ks & 3), never the stage the next loads overwrite.
+    MUON_WAIT_VM(8);
+    __builtin_amdgcn_s_barrier();
+    MUON_GLOAD(ks + 3 < kl ? ks + 3 : kl);
+    MUON_FRAGS(1, ks, 1);
+    MUON_MFMA(0);
+    MUON_FRAGS(0, ks + 1, 0);  // stage of ks + 1 (re-reads the last stage at the end)
+    MUON_MFMA(1);
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // global->LDS loads first
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        ra[q] = *reinterpret_cast<const u32x4 *>(pa + prow + int64_t(q) * 32 * ld + k0);
-        rb[q] = *reinterpret_cast<const u32x4 *>(qa + qrow + int64_t(q) * 32 * ld + k0);
-      }
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    if (ks >= 0) {
-      const char *A = smem + (ks & 1) * 2 * kOpBytes;
-      const char *B = A + kOpBytes;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ch = ((kk * 2 + fh) ^ fx) << 4;
-        bf16x8 af[4], bfr[4];
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-          af[bi] = *reinterpret_cast<const bf16x8 *>(A + (wm * 128 + bi * 32 + fr) * 128 + ch);
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
-          bfr[bj] = *reinterpret_cast<const bf16x8 *>(B + (wn * 128 + bj * 32 + fr) * 128 + ch);
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-          for (int bj = 0; bj < 4; ++bj)
-            acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bfr[bj], acc[bi][bj], 0, 0, 0);
-      }
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    if (ks + 1 < nk) {
-      // stage ks + 1 lives in buffer (ks + 1) & 1; its previous contents
-      // (step ks - 1) were consumed before the barrier that ended step ks - 1
-      char *A = smem + ((ks + 1) & 1) * 2 * kOpBytes;
-      char *B = A + kOpBytes;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        *reinterpret_cast<u32x4 *>(A + q * 4096 + sw_off) = ra[q];
-        *reinterpret_cast<u32x4 *>(B + q * 4096 + sw_off) = rb[q];
-      }
-    }
-    __syncthreads();
   }
+  MUON_WAIT_VM(0);  // no load may still target LDS when the workgroup ends
+#undef MUON_GLOAD
+#undef MUON_FRAGS
+#undef MUON_MFMA
+#undef MUON_WAIT_VM
 
   // ---------------- epilogues ----------------
-  GemmEpilogue<PHASE> ep;
-  ep.mp = mp;
-  ep.np = np;
-  ep.ib = i0 + wm * 128 + fh * 4;
-  ep.jb = j0 + wn * 128 + fr;
-  ep.diag = ti.I == ti.J;
-  ep.a = args.a;
-  ep.b = args.b;
-  ep.c = args.c;
-  ep.ahi = reinterpret_cast<bf16 *>(blk + S.off_ahi);
-  ep.alo = reinterpret_cast<bf16 *>(blk + S.off_alo);
-  ep.bm = reinterpret_cast<bf16 *>(blk + S.off_b);
-  ep.xt = reinterpret_cast<const bf16 *>(blk + S.off_xt[args.src]);
-  ep.ya = reinterpret_cast<bf16 *>(blk + S.off_xa[args.src ^ 1]);
-  ep.yt = reinterpret_cast<bf16 *>(blk + S.off_xt[args.src ^ 1]);
-  ep.bdiag = reinterpret_cast<float *>(blk + S.off_bdiag);
-  ep.scale = 1.f;
-  if (args.first) {
-    const float *sc = reinterpret_cast<const float *>(blk + S.off_scale);
-    ep.scale = PHASE == kGram ? sc[1] : (PHASE == kBX ? sc[0] : 1.f);
+  __syncthreads();  // every wave is done with the LDS ring
+  const EpiCoord ec{wm * 128 + fh * 4, wn * 128 + fr};
+  const bool diag = (PHASE != kBX) && ti.I == ti.J;
+  float *scale_p = reinterpret_cast<float *>(blk + S.off_scale);
+
+  if (PHASE == kGram) {
+    // A = s' X X^T as bf16 hi + lo. Each output tile passes through LDS in
+    // its own row order: A[j][i] (8-byte writes) for the mirror tile (J, I),
+    // A[i][j] for the tile (I, J); a diagonal tile leaves once, symmetrized.
+    const float sg = args.first ? scale_p[1] : 1.f;
+    for_blocks(acc, [&](f32x16 &a, int, int) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = a[r] * sg;
+        a[r] = __uint_as_float(pack_bf16(x, x - float(bf16(x))));
+      }
+    });
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {  // 0: hi (bits 16..31), 1: lo
+      bf16 *dst = reinterpret_cast<bf16 *>(blk + (half ? S.off_alo : S.off_ahi));
+      const int shift = half ? 0 : 16;
+      fill_tile<true>(smem, acc, ec, shift);
+      lds_barrier();
+      if (diag) {
+        tile_store_sym(smem, dst, mp, i0, j0, tid);
+      } else {
+        tile_store(smem, dst, mp, j0, i0, tid);  // mirror tile (J, I)
+        lds_barrier();
+        fill_tile<false>(smem, acc, ec, shift);
+        lds_barrier();
+        tile_store(smem, dst, mp, i0, j0, tid);  // tile (I, J)
+      }
+      lds_barrier();
+    }
+  } else if (PHASE == kAA) {
+    // B = b A + c A A. A's tile comes in from the mirror position (J, I),
+    // whose rows are the columns of tile (I, J): A[i][j] = A[j][i].
+    const bf16 *Ah = reinterpret_cast<const bf16 *>(blk + S.off_ahi);
+    const bf16 *Al = reinterpret_cast<const bf16 *>(blk + S.off_alo);
+    for_blocks(acc, [&](f32x16 &a, int, int) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[r] *= args.c;
+    });
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      tile_load(smem, half ? Al : Ah, mp, j0, i0, tid);
+      lds_barrier();
+      for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const bf16x4 h4 = get_trans(smem, ec, bi, bj, r4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a[r4 * 4 + q] = fmaf(args.b, float(h4[q]), a[r4 * 4 + q]);
+        }
+      });
+      lds_barrier();
+    }
+    // the diagonal of B stays in float32 (bdiag); B stores it as zero
+    float *bdiag = reinterpret_cast<float *>(blk + S.off_bdiag);
+    bf16 *Bm = reinterpret_cast<bf16 *>(blk + S.off_b);
+    for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float x = a[r4 * 4 + q];
+          if (diag && ec.ib + bi * 32 + r4 * 8 + q == ec.jb + bj * 32) {
+            bdiag[i0 + ec.jb + bj * 32] = x;
+            x = 0.f;
+          }
+          a[r4 * 4 + q] = __uint_as_float(pack_bf16(0.f, x));
+        }
+    });
+    fill_tile<true>(smem, acc, ec, 0);
+    lds_barrier();
+    if (diag) {
+      tile_store_sym(smem, Bm, mp, i0, j0, tid);
+    } else {
+      tile_store(smem, Bm, mp, j0, i0, tid);  // mirror tile (J, I)
+      lds_barrier();
+      fill_tile<false>(smem, acc, ec, 0);
+      lds_barrier();
+      tile_store(smem, Bm, mp, i0, j0, tid);  // tile (I, J)
+    }
+  } else {
+    // X' = s'' ((a + B_ii) X + B_offdiag X): X's tile comes in from X^T
+    // (rows j), the result leaves as X'^T (rows j) and X' (rows i)
+    const float sx = args.first ? scale_p[0] : 1.f;
+    const float *bdiag = reinterpret_cast<const float *>(blk + S.off_bdiag);
+    const bf16 *Xt = reinterpret_cast<const bf16 *>(blk + S.off_xt[args.src]);
+    bf16 *Ya = reinterpret_cast<bf16 *>(blk + S.off_xa[args.src ^ 1]);
+    bf16 *Yt = reinterpret_cast<bf16 *>(blk + S.off_xt[args.src ^ 1]);
+    tile_load(smem, Xt, mp, j0, i0, tid);
+    lds_barrier();
+    for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ti_ = ec.ib + bi * 32 + r4 * 8;
+        const bf16x4 x4 = get_trans(smem, ec, bi, bj, r4);
+        const float4 d4 = *reinterpret_cast<const float4 *>(bdiag + i0 + ti_);
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float o = sx * fmaf(args.a + dd[q], float(x4[q]), a[r4 * 4 + q]);
+          a[r4 * 4 + q] = __uint_as_float(pack_bf16(0.f, o));
+        }
+      }
+    });
+    lds_barrier();  // every lane has read its X values before the tile is overwritten
+    fill_tile<true>(smem, acc, ec, 0);
+    lds_barrier();
+    tile_store(smem, Yt, mp, j0, i0, tid);  // X'^T rows j
+    lds_barrier();
+    fill_tile<false>(smem, acc, ec, 0);
+    lds_barrier();
+    tile_store(smem, Ya, np, i0, j0, tid);  // X' rows i
   }
-  run_epilogue(acc, ep, std::make_integer_sequence<int, 16>{});
 }
 
 // ---------------------------------------------------------------------------

@@ -93,6 +93,23 @@ def cpu_baseline(wl, budget_s):
     }
 
 
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` recorded in the profile summary for this
+    workload, or None when there is none or the kernel source changed since."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"muon_step_{workload}.md")
+    src = os.path.join(ROOT, "muon_newton_schulz_03_amd", "csrc", "kernels.hip")
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    text = open(path).read()
+    m = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not m or m.group(1) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    m = re.search(r"^traffic_bytes_per_launch " + re.escape(kernel) + r": (\d+)$", text, re.M)
+    return int(m.group(1)) if m else None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -205,7 +222,9 @@ def main():
             "peak": round(PEAK_BF16_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": (recorded_traffic(wl.name, {"gram": "gemm_bf16_kernel<0>", "aa": "gemm_bf16_kernel<1>",
+                                                   "bx": "gemm_bf16_kernel<2>"}[dom])
+                        if args.pack == "cost" and args.workspace_gb == 32.0 else None),
             "flops_per_launch": fl_launch,
             "avg_launch_ms": round(avg_ms, 4),
         }

@@ -71,8 +71,14 @@ __device__ inline TileInfo decode_tile(const GemmArgs &a, int tile, bool syrk) {
     while (J * (J + 1) / 2 > u) --J;
     I = u - J * (J + 1) / 2;
   } else {
-    I = u / S.tn;
-    J = u - I * S.tn;
+    // B X tiles go in blocks of (all row panels) x (jblock column panels):
+    // about 32 consecutive tiles, one XCD's worth, then share every panel of
+    // B and jblock panels of X, so both stay in that XCD's L2
+    const int tI = S.mp / (S.np / S.tn);
+    const int per = tI * S.jblock;
+    const int jb = u / per, r = u - jb * per;
+    I = r % tI;
+    J = jb * S.jblock + r / tI;
   }
   return {s, view, I, J};
 }

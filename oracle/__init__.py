@@ -14,4 +14,5 @@ from .muon_oracle import (  # noqa: F401
     newton_schulz,
     newton_schulz_blockwise,
     muon_step,
+    newton_schulz_iteration_rows,
 )

@@ -155,3 +155,26 @@ def muon_step(W, G, M, lr, beta, nesterov=False, iters=5,
         O = newton_schulz(X, iters, coeffs, eps, dtype)
     W_new = np.asarray(W, dtype=dtype) - dtype(lr) * O
     return O, M_new, W_new
+
+
+def newton_schulz_iteration_rows(X, rows, coeffs=DEFAULT_COEFFS, scale=1.0,
+                                 dtype=np.float64):
+    """Selected rows of one Newton-Schulz iteration applied to ``scale * X``
+    (X already oriented wide): rows of ``a Y + (b A + c A A) Y`` with
+    ``Y = scale * X`` and ``A = Y Y^T``.
+
+    Row i needs only matrix-vector products: ``A[i,:] = Y Y[i]``,
+    ``(A A)[i,:] = Y (Y^T A[i,:])`` and ``(B Y)[i] = Y^T B[i,:]``. This lets a
+    check recompute one iteration exactly for a few rows of a matrix too large
+    for the whole-matrix oracle.
+    """
+    a, b, c = (dtype(v) for v in coeffs)
+    Y = np.asarray(X, dtype=dtype) * dtype(scale)
+    out = []
+    for i in rows:
+        y = Y[i]
+        Ai = Y @ y
+        AAi = Y @ (Y.T @ Ai)
+        Bi = b * Ai + c * AAi
+        out.append(a * y + Y.T @ Bi)
+    return np.array(out)

@@ -306,6 +306,29 @@ def test_muon_step_blockwise_uses_blocks():
 
 
 # ---------------------------------------------------------------------------
+# row-sampled single iteration
+# ---------------------------------------------------------------------------
+
+def test_iteration_rows_match_closed_form():
+    # one iteration of the normalized matrix is the closed form with k = 1
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((12, 30))
+    s = 1.0 / (np.linalg.norm(X) + EPS)
+    rows = [0, 5, 11]
+    got = oracle.newton_schulz_iteration_rows(X, rows, scale=s)
+    assert relF(got, closed_form(X, 1)[rows]) < 1e-13
+
+
+def test_iteration_rows_second_iteration():
+    # applied to the first iterate it gives rows of the second (closed form)
+    rng = np.random.default_rng(22)
+    X = rng.standard_normal((9, 20))
+    X1 = closed_form(X, 1)
+    got = oracle.newton_schulz_iteration_rows(X1, [0, 8])
+    assert relF(got, closed_form(X, 2)[[0, 8]]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
 # the pins catch planted mistakes
 # ---------------------------------------------------------------------------
 

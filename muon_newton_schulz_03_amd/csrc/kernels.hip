@@ -612,21 +612,28 @@ void gemm_bf16_kernel(const GemmArgs args) {
       });
       lds_barrier();
     }
-    // the diagonal of B stays in float32 (bdiag); B stores it as zero
+    // The diagonal of B stays in float32 (bdiag); B stores it as zero. Only
+    // blocks (bb, bb) of the waves with wm == wn in a diagonal tile hold
+    // diagonal elements: row 8 r4 + 4 fh + q equals column fr for the lanes
+    // with fh == (fr >> 2) & 1, in register (fr >> 3) * 4 + (fr & 3).
     float *bdiag = reinterpret_cast<float *>(blk + S.off_bdiag);
     bf16 *Bm = reinterpret_cast<bf16 *>(blk + S.off_b);
-    for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+    if (diag && wm == wn) {
+      const bool holder = fh == ((fr >> 2) & 1);
+      const int rr = (fr >> 3) * 4 + (fr & 3);
+      for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+        if (bi != bj) return;
+        float x = 0.f;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
+        for (int r = 0; r < 16; ++r) x = r == rr ? a[r] : x;
+        if (holder) bdiag[i0 + wm * 128 + bi * 32 + fr] = x;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float x = a[r4 * 4 + q];
-          if (diag && ec.ib + bi * 32 + r4 * 8 + q == ec.jb + bj * 32) {
-            bdiag[i0 + ec.jb + bj * 32] = x;
-            x = 0.f;
-          }
-          a[r4 * 4 + q] = __uint_as_float(pack_bf16(0.f, x));
-        }
+        for (int r = 0; r < 16; ++r) a[r] = (holder && r == rr) ? 0.f : a[r];
+      });
+    }
+    for_blocks(acc, [&](f32x16 &a, int, int) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, a[r]));
     });
     fill_tile<true>(smem, acc, ec, 0);
     lds_barrier();

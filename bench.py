@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--workload", default="kimi_moe_layer")
     p.add_argument("--workspace-gb", type=float, default=32.0)
     p.add_argument("--pack", choices=["cost", "rr"], default="cost")
+    p.add_argument("--aa", choices=["plain", "split"], default="plain",
+                   help="A*A from bf16(A) (default) or from A as bf16 hi + lo")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the CPU-oracle sample (0 disables it)")
     p.add_argument("--no-phase-timing", action="store_true")
@@ -129,6 +131,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     mode = (mu.MUON_PACK_COST if args.pack == "cost" else mu.MUON_PACK_RR)
+    mode |= mu.MUON_AA_SPLIT if args.aa == "split" else mu.MUON_AA_PLAIN
     if wl.col_blocks > 1:
         mode |= mu.MUON_NS_BLOCKWISE
     print(f"[bench] workload {wl.name}: {len(wl.shapes)} matrices; generating inputs", file=sys.stderr,
@@ -193,6 +196,7 @@ def main():
             "col_blocks": wl.col_blocks,
             "iters": wl.iters,
             "pack": args.pack,
+            "aa": args.aa,
             "workspace_gib": round(ws_bytes / 2**30, 2),
             "groups": len(plan["chunks"]),
         },
@@ -224,7 +228,8 @@ def main():
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": (recorded_traffic(wl.name, {"gram": "gemm_bf16_kernel<0>", "aa": "gemm_bf16_kernel<1>",
                                                    "bx": "gemm_bf16_kernel<2>"}[dom])
-                        if args.pack == "cost" and args.workspace_gb == 32.0 else None),
+                        if args.pack == "cost" and args.aa == "plain" and args.workspace_gb == 32.0
+                        else None),
             "flops_per_launch": fl_launch,
             "avg_launch_ms": round(avg_ms, 4),
         }

@@ -23,7 +23,8 @@
  *   - The precision path follows the dtype: all-float32 matrices run the
  *     float32 path (float32 arithmetic throughout); all-bfloat16 matrices run
  *     the bfloat16 matrix-core path (bf16 operands, fp32 accumulation, fp32
- *     epilogues, bf16 intermediates; A*A uses A split into bf16 hi + lo).
+ *     epilogues, bf16 intermediates; A*A from bf16(A) by default, from A
+ *     split into bf16 hi + lo with MUON_AA_SPLIT).
  *   - NaN and Inf in the inputs propagate; nothing is masked.
  *   - State set by muon_set_* is per host thread.
  */
@@ -76,9 +77,11 @@ typedef struct muon_mat {
 #define MUON_PACK_RR 0x000u      /* matrices enter the grouped launches in the
                                     order given (round robin)                */
 #define MUON_PACK_COST 0x010u    /* ... in descending cost order             */
-#define MUON_AA_SPLIT 0x000u     /* A*A from bf16 hi/lo halves of A (3 products) */
-#define MUON_AA_PLAIN 0x100u     /* A*A from bf16-rounded A (1 product);
-                                    diagnostic, less accurate                */
+#define MUON_AA_PLAIN 0x000u     /* A*A and b A from bf16-rounded A
+                                    (1 product)                              */
+#define MUON_AA_SPLIT 0x100u     /* A*A and b A from A as bf16 hi + lo halves
+                                    (3 products: hi hi + hi lo + lo hi);
+                                    about 1.3x less error, 3x the A*A work   */
 
 /* Limits: the smaller dimension of a matrix (or block) at most 32768, the
  * larger at most 4194304; iters at most 64; n_mats at most 1048576. */
@@ -102,6 +105,8 @@ typedef struct muon_mat {
  *           All descriptors must share one dtype and must not overlap.
  *   iters   >= 0; 0 means normalize only.
  *   coeffs  host array {a, b, c}; NULL means {3.4445, -4.7750, 2.0315}.
+ *           All finite, c != 0 and b / c finite (B is formed as
+ *           c (A A + (b / c) A)); otherwise MUON_ERR_INVALID_ARG.
  *   mode    MUON_NS_* | MUON_PACK_* | MUON_AA_* bits.
  *   eps     taken from muon_set_step_options (default 1e-7).
  * n_mats == 0 is a no-op returning MUON_OK.
@@ -157,8 +162,10 @@ muon_status muon_set_workspace(void *device_ptr, size_t bytes);
 
 /* Options used by muon_step (and eps by muon_ns_batched) on this thread.
  * Defaults: iters 5, coeffs {3.4445, -4.7750, 2.0315}, eps 1e-7,
- * mode MUON_NS_FULL | MUON_PACK_COST | MUON_AA_SPLIT. coeffs NULL keeps the
- * current coefficients. eps must be finite and >= 0. */
+ * mode MUON_NS_FULL | MUON_PACK_COST | MUON_AA_PLAIN. coeffs NULL keeps the
+ * current coefficients; non-NULL coefficients follow the rule of
+ * muon_ns_batched (finite, c != 0, b / c finite). eps must be finite and
+ * >= 0. */
 muon_status muon_set_step_options(int32_t iters, const float coeffs[3], float eps,
                                   uint32_t mode);
 

@@ -32,11 +32,11 @@ MUON_NS_FULL = 0x000
 MUON_NS_BLOCKWISE = 0x001
 MUON_PACK_RR = 0x000
 MUON_PACK_COST = 0x010
-MUON_AA_SPLIT = 0x000
-MUON_AA_PLAIN = 0x100
+MUON_AA_PLAIN = 0x000
+MUON_AA_SPLIT = 0x100
 
 DEFAULT_COEFFS = (3.4445, -4.7750, 2.0315)
-DEFAULT_MODE = MUON_NS_FULL | MUON_PACK_COST | MUON_AA_SPLIT
+DEFAULT_MODE = MUON_NS_FULL | MUON_PACK_COST | MUON_AA_PLAIN
 
 EXPORTED = (
     "muon_ns_batched", "muon_step", "muon_set_stream", "muon_workspace_size",

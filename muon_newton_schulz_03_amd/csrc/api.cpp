@@ -19,7 +19,7 @@ struct State {
   int32_t iters = 5;
   float coeffs[3] = {3.4445f, -4.7750f, 2.0315f};
   float eps = 1e-7f;
-  uint32_t mode = MUON_NS_FULL | MUON_PACK_COST | MUON_AA_SPLIT;
+  uint32_t mode = MUON_NS_FULL | MUON_PACK_COST | MUON_AA_PLAIN;
   std::string err;
 };
 
@@ -72,7 +72,13 @@ muon_status ok() {
   return MUON_OK;
 }
 
-bool finite3(const float *c) { return std::isfinite(c[0]) && std::isfinite(c[1]) && std::isfinite(c[2]); }
+// The A*A kernel forms B = c (A A + (b / c) A), so c must be nonzero and
+// b / c finite.
+bool coeffs_ok(const float *c) {
+  return std::isfinite(c[0]) && std::isfinite(c[1]) && std::isfinite(c[2]) && c[2] != 0.f &&
+         std::isfinite(c[1] / c[2]);
+}
+constexpr const char *kCoeffMsg = "coefficients must be finite, with c != 0 and b / c finite";
 
 struct Sources {
   const muon_mat *data = nullptr;  // muon_ns_batched
@@ -105,8 +111,9 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
     ga.a = coeffs[0];
     ga.b = coeffs[1];
     ga.c = coeffs[2];
+    ga.r = coeffs[1] / coeffs[2];
     ga.eps = eps;
-    ga.aa_plain = (plan.mode & MUON_AA_PLAIN) ? 1 : 0;
+    ga.aa_plain = (plan.mode & MUON_AA_SPLIT) ? 0 : 1;
     ga.remap = 1;
     int32_t view_begin = 0;
     for (size_t s = 0; s < ch.segs.size(); ++s) {
@@ -115,10 +122,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       GemmSeg &g = ga.seg[s];
       g.base = ws + sg.base;
       g.stride = int64_t(sg.stride);
-      for (int p = 0; p < 2; ++p) {
-        g.off_xa[p] = int64_t(L.xa[p]);
-        g.off_xt[p] = int64_t(L.xt[p]);
-      }
+      for (int p = 0; p < 2; ++p) g.off_xa[p] = int64_t(L.xa[p]);
       g.off_ahi = int64_t(L.ahi);
       g.off_alo = int64_t(L.alo);
       g.off_b = int64_t(L.b);
@@ -186,14 +190,13 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
         e.vec = (step ? rows16(e.g, e.ld_g) : 0) | (rows16(e.m, e.ld_m) << 1) | (step ? rows16(e.w, e.ld_w) << 2 : 0);
         e.blk = blocks[k];
         const int buf = prep ? 0 : fin;
-        e.off_direct = int64_t(v.tall ? L.xt[buf] : L.xa[buf]);
-        e.off_trans = int64_t(v.tall ? L.xa[buf] : L.xt[buf]);
+        e.off_x = int64_t(L.xa[buf]);
         e.off_part = int64_t(L.partials);
         e.off_scale = int64_t(L.scale);
         e.rows = int32_t(v.rows);
         e.cols = int32_t(v.cols);
-        e.pitch_direct = int32_t(v.tall ? v.mp : v.np);
-        e.pitch_trans = int32_t(v.tall ? v.np : v.mp);
+        e.pitch_x = int32_t(v.np);
+        e.tall = v.tall ? 1 : 0;
         int64_t tr, tcn;
         if (prep) {  // whole padded extent, so the padding is written as zeros
           tr = (v.tall ? v.np : v.mp) / kElemTile;
@@ -257,7 +260,7 @@ muon_status muon_ns_batched(const muon_mat *descs, int32_t n_mats, int32_t iters
   static const float kDefault[3] = {3.4445f, -4.7750f, 2.0315f};
   const float *cf = coeffs ? coeffs : kDefault;
   if (!validate_mode(mode, &err) || !check_iters(iters, &err)) return fail(err);
-  if (!finite3(cf)) return fail(MUON_ERR_INVALID_ARG, "coefficients must be finite");
+  if (!coeffs_ok(cf)) return fail(MUON_ERR_INVALID_ARG, kCoeffMsg);
   if (!validate_descs(descs, n_mats, mode, "descs", &err)) return fail(err);
   if (n_mats == 0) return ok();
   const muon_mat *arrays[1] = {descs};
@@ -333,7 +336,7 @@ muon_status muon_set_step_options(int32_t iters, const float coeffs[3], float ep
   Error err;
   if (!check_iters(iters, &err) || !validate_mode(mode, &err)) return fail(err);
   if (!std::isfinite(eps) || eps < 0.f) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  if (coeffs && !finite3(coeffs)) return fail(MUON_ERR_INVALID_ARG, "coefficients must be finite");
+  if (coeffs && !coeffs_ok(coeffs)) return fail(MUON_ERR_INVALID_ARG, kCoeffMsg);
   g_state.iters = iters;
   if (coeffs) std::memcpy(g_state.coeffs, coeffs, sizeof g_state.coeffs);
   g_state.eps = eps;

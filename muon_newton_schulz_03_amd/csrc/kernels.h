@@ -1,9 +1,10 @@
 // Launch arguments shared by the host runtime and the HIP kernels.
 //
 // Workspace: every view (a whole matrix, or a column block in blockwise mode)
-// owns one block of the caller's workspace holding X and X^T (ping-pong), the
-// Gram matrix A (bf16 hi/lo halves, or float32), B = b A + c A A, the
-// per-tile partial sums of squares and its scale s = 1/(||X||_F + eps).
+// owns one block of the caller's workspace holding X (wide orientation,
+// row-major, ping-pong), the Gram matrix A (bf16 hi/lo halves, or float32),
+// B = b A + c A A, the per-tile partial sums of squares and its scale
+// s = 1/(||X||_F + eps).
 // Views of one padded shape sit at a uniform stride ("segment"), so a grouped
 // launch needs only a handful of segment descriptors in its kernel arguments.
 #pragma once
@@ -32,12 +33,11 @@ struct ElemView {
   void *w;        // weight view (finish step)
   int64_t ld_g, ld_m, ld_w;  // elements
   char *blk;                 // workspace block of the view
-  int64_t off_direct;        // buffer in the user's orientation (X if wide, X^T if tall)
-  int64_t off_trans;         // the other orientation (prep only)
+  int64_t off_x;             // X (wide orientation: X^T of the user's view if tall)
   int64_t off_part, off_scale;
   int32_t rows, cols;        // view shape, user orientation
-  int32_t pitch_direct;      // row pitch (elements) of the direct buffer
-  int32_t pitch_trans;       // row pitch of the transposed buffer
+  int32_t pitch_x;           // row pitch (elements) of X
+  int32_t tall;              // user view is X^T: prep and finish transpose through LDS
   int32_t tiles_c;           // 64-wide tiles along the user's columns
   int32_t tile_begin;        // first tile of this view in the launch
   int32_t vec;               // bit 0/1/2: g/m/w rows start on 16-byte boundaries
@@ -57,7 +57,7 @@ struct ElemArgs {
 struct GemmSeg {
   char *base;
   int64_t stride;
-  int64_t off_xa[2], off_xt[2], off_ahi, off_alo, off_b, off_bdiag, off_part, off_scale;
+  int64_t off_xa[2], off_ahi, off_alo, off_b, off_bdiag, off_part, off_scale;
   int32_t mp, np;
   int32_t count;
   int32_t tiles_per_view;
@@ -75,9 +75,10 @@ struct GemmArgs {
   int32_t total_tiles;
   int32_t src;      // X buffer read this iteration; the product goes to src ^ 1
   int32_t first;    // first iteration: apply the normalization scale
-  int32_t aa_plain; // A*A from bf16(A) only
+  int32_t aa_plain; // A*A and b A from bf16(A) only (no lo half of A)
   int32_t remap;    // XCD-aware tile order
   float a, b, c;
+  float r;          // b / c: the A*A kernel adds r A inside its K loop, then scales by c
   float eps;
 };
 

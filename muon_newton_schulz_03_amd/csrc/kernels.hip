@@ -1,18 +1,18 @@
 // HIP kernels of the Muon step for CDNA4 (gfx950).
 //
 // Per group of views (whole matrices or column blocks), in stream order:
-//   elem_kernel (prep)      momentum M <- beta M + G, Newton-Schulz source X0,
-//                           X0 and X0^T written zero-padded into the
-//                           workspace, per-tile partial sums of squares.
+//   elem_kernel (prep)      momentum M <- beta M + G, Newton-Schulz source X0
+//                           written zero-padded into the workspace in wide
+//                           orientation, per-tile partial sums of squares.
 //   norm_finalize_kernel    s = 1/(||X0||_F + eps) from the partial sums.
 //   iters x { gemm <Gram>   A = s' X X^T (upper-triangle tiles, mirrored),
 //                           stored as bf16 hi + lo;
 //             gemm <AA>     B = b A + c A A (upper tiles, mirrored), A A from
 //                           hi*hi + hi*lo + lo*hi;
-//             gemm <BX>     X' = s'' (a X + B X), stored as X' and X'^T }
+//             gemm <BX>     X' = s'' (a X + B X) }
 //   elem_kernel (finish)    data <- O, or W <- W - lr O.
 // s' = s^2 and s'' = s in the first iteration (the normalization is folded
-// into the first Gram and the first B X epilogue), 1 afterwards.
+// into the first Gram and the first B X), 1 afterwards.
 //
 // Three products per iteration, the first two symmetric rank-k products
 // (SYRK) with only upper-triangle tiles computed and the diagonal tiles in
@@ -20,10 +20,10 @@
 // (zh translation, wiki.whaty.org), sections "Distributed mode" and
 // "SYRK 和融合的 all-reduce".
 //
-// All three products are "NT" contractions C[i][j] = sum_k P[i][k] Q[j][k]
-// with both operands K-contiguous: the Gram reads rows of X twice, A*A reads
-// rows of the symmetric A twice, and B X reads rows of B and rows of X^T --
-// which is why every B X epilogue also writes X'^T.
+// The Gram and A*A are "NT" contractions C[i][j] = sum_k P[i][k] Q[j][k]
+// over K-contiguous rows (of X, of the symmetric A). B X reads rows i of the
+// symmetric B the same way and rows k of X through transposing LDS reads, so
+// X lives in one row-major layout only.
 #include <hip/hip_runtime.h>
 
 #include <utility>
@@ -35,7 +35,6 @@ namespace {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -142,9 +141,11 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
   const int tr = u / Vw.tiles_c, tc = u - (u / Vw.tiles_c) * Vw.tiles_c;
   const int kind = args.kind;
 
+  T *X = reinterpret_cast<T *>(Vw.blk + Vw.off_x);
+  const int64_t px = Vw.pitch_x;
   if (kind == kPrepNs || kind == kPrepStep) {
-    T *direct = reinterpret_cast<T *>(Vw.blk + Vw.off_direct);
-    T *trans = reinterpret_cast<T *>(Vw.blk + Vw.off_trans);
+    // X0 in wide orientation: this tile's rows as they are, or (tall view)
+    // transposed through the LDS tile
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
@@ -171,16 +172,18 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
         ss = fmaf(xf, xf, ss);
         tile[row][cc * V + e] = xv.e[e];
       }
-      *reinterpret_cast<Vec16<T> *>(direct + int64_t(gr) * Vw.pitch_direct + gc) = xv;
+      if (!Vw.tall) *reinterpret_cast<Vec16<T> *>(X + int64_t(gr) * px + gc) = xv;
     }
-    __syncthreads();
+    if (Vw.tall) {
+      __syncthreads();
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int c = tid + 256 * q, trow = c / CPR, tcc = c % CPR;
-      Vec16<T> tv;
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + 256 * q, trow = c / CPR, tcc = c % CPR;
+        Vec16<T> tv;
 #pragma unroll
-      for (int e = 0; e < V; ++e) tv.e[e] = tile[tcc * V + e][trow];
-      *reinterpret_cast<Vec16<T> *>(trans + int64_t(tc * 64 + trow) * Vw.pitch_trans + tr * 64 + tcc * V) = tv;
+        for (int e = 0; e < V; ++e) tv.e[e] = tile[tcc * V + e][trow];
+        *reinterpret_cast<Vec16<T> *>(X + int64_t(tc * 64 + trow) * px + tr * 64 + tcc * V) = tv;
+      }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
@@ -188,17 +191,34 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
     __syncthreads();
     if (tid == 0) reinterpret_cast<float *>(Vw.blk + Vw.off_part)[u] = (red[0] + red[1]) + (red[2] + red[3]);
   } else {
-    const T *O = reinterpret_cast<const T *>(Vw.blk + Vw.off_direct);
     const float sf = args.final_scale ? reinterpret_cast<const float *>(Vw.blk + Vw.off_scale)[0] : 1.f;
+    if (Vw.tall) {
+      // the user's tile (tr, tc) is X[tc*64 .., tr*64 ..] transposed: stage
+      // that block of X in LDS with coalesced row reads (inside the padded
+      // extent of X, so no bounds checks)
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + 256 * q, row = c / CPR, cc = c % CPR;
+        const Vec16<T> v = *reinterpret_cast<const Vec16<T> *>(X + int64_t(tc * 64 + row) * px + tr * 64 + cc * V);
+#pragma unroll
+        for (int e = 0; e < V; ++e) tile[row][cc * V + e] = v.e[e];
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int c = tid + 256 * q, row = c / CPR, cc = c % CPR;
       const int gr = tr * 64 + row, gc = tc * 64 + cc * V;
       if (gr >= Vw.rows || gc >= Vw.cols) continue;
-      const Vec16<T> ov = *reinterpret_cast<const Vec16<T> *>(O + int64_t(gr) * Vw.pitch_direct + gc);
       float o[V];
+      if (Vw.tall) {
 #pragma unroll
-      for (int e = 0; e < V; ++e) o[e] = float(ov.e[e]) * sf;
+        for (int e = 0; e < V; ++e) o[e] = float(tile[cc * V + e][row]) * sf;
+      } else {
+        const Vec16<T> ov = *reinterpret_cast<const Vec16<T> *>(X + int64_t(gr) * px + gc);
+#pragma unroll
+        for (int e = 0; e < V; ++e) o[e] = float(ov.e[e]) * sf;
+      }
       if (kind == kFinishNs) {
         store_row_chunk<T>(Vw.m, Vw.ld_m, gr, gc, Vw.rows, Vw.cols, Vw.vec & 2, o);
       } else {
@@ -242,13 +262,13 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const GemmArgs args)
 // bf16 matrix-core kernel: 256x256 output tile, 4 waves (2x2), each wave
 // 128x128 = 4x4 blocks of v_mfma_f32_32x32x16_bf16.
 //
-// Operands stream through a 4-stage LDS ring (stage = 256 rows x 32 k of
-// both operands, 2 x 16 KiB). Global memory goes straight to LDS with
-// global_load_lds_dwordx4 (each lane's 16 bytes land at LDS base + 16 * lane),
-// issued three K steps ahead, so no registers hold staged data and the load
-// latency hides behind three steps of matrix work. One barrier per K step:
-// after it, step ks + 1 is visible to every wave and the stage of step
-// ks - 1 is free for the loads of step ks + 3.
+// Operands stream through a 5-stage LDS ring (stage = 256 rows x 32 k of
+// both operands, 2 x 16 KiB; 160 KiB in all). Global memory goes straight to
+// LDS with global_load_lds_dwordx4 (each lane's 16 bytes land at LDS base +
+// 16 * lane), issued four K steps ahead, so no registers hold staged data and
+// the load latency hides behind four steps of matrix work. One barrier per K
+// step: after it, step ks + 1 is visible to every wave and the stage of step
+// ks - 1 is free for the loads of step ks + 4.
 //
 // A 64-byte LDS row holds four 16-byte chunks of k, XOR-swizzled by
 // ((row >> 2) & 3): the 16 lanes of a fragment-read group (16 consecutive
@@ -261,18 +281,17 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const GemmArgs args)
 // C[8 (r >> 2) + 4 (l >> 5) + (r & 3)][l & 31].
 // ---------------------------------------------------------------------------
 
-constexpr int kBM = 256, kBK = 32, kStages = 4;
+constexpr int kBM = 256, kBK = 32, kStages = 5;
 constexpr int kOpBytes = kBM * kBK * 2;          // one operand tile, one stage (16 KiB)
 constexpr int kStageBytes = 2 * kOpBytes;        // both operands
 
 // ---------------------------------------------------------------------------
-// Epilogues. After the K loop the LDS ring (128 KiB) holds one 256 x 256 bf16
+// Epilogues. After the K loop the LDS ring holds one 256 x 256 bf16 (128 KiB)
 // tile: 512-byte rows whose 16-byte chunks are XOR-swizzled by
 // row ^ ((row & 3) << 2) (mod 32), which spreads both 32 consecutive rows at
 // one column and 4 consecutive rows at 8 consecutive columns over the banks.
 // Accumulators go to that tile in whichever orientation a pass needs, and the
-// tile then leaves as coalesced 16-byte row stores (and arrives the same way
-// when an epilogue needs a tile of another matrix).
+// tile then leaves as coalesced 16-byte row stores.
 // ---------------------------------------------------------------------------
 
 __device__ inline int tile_chunk(int row, int c) { return (c ^ row ^ ((row & 3) << 2)) & 31; }
@@ -300,15 +319,6 @@ __device__ inline void tile_store(const char *smem, bf16 *dst, int64_t pitch, in
     *reinterpret_cast<u32x4 *>(dst + int64_t(row0 + row) * pitch + col0 + c * 8) = v;
   }
 }
-__device__ inline void tile_load(char *smem, const bf16 *src, int64_t pitch, int row0, int col0, int tid) {
-#pragma unroll 8
-  for (int k = 0; k < 32; ++k) {
-    const int u = tid + 256 * k, row = u >> 5, c = u & 31;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + int64_t(row0 + row) * pitch + col0 + c * 8);
-    *reinterpret_cast<u32x4 *>(smem + row * 512 + (tile_chunk(row, c) << 4)) = v;
-  }
-}
-
 // Barrier for LDS hand-offs inside the epilogue: waits for this wave's LDS
 // operations only, not for its global stores (a full __syncthreads() fence
 // would wait for every store of the previous pass to land).
@@ -387,11 +397,6 @@ __device__ inline void put_trans(char *smem, const EpiCoord &e, int bi, int bj, 
   const int tj = e.jb + bj * 32, ti = e.ib + bi * 32 + r4 * 8;
   *reinterpret_cast<u32x2 *>(smem + tile_off(tj, ti)) = v;
 }
-__device__ inline bf16x4 get_trans(const char *smem, const EpiCoord &e, int bi, int bj, int r4) {
-  const int tj = e.jb + bj * 32, ti = e.ib + bi * 32 + r4 * 8;
-  return *reinterpret_cast<const bf16x4 *>(smem + tile_off(tj, ti));
-}
-
 template <bool TRANS>
 __device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const EpiCoord &e, int shift) {
   for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
@@ -406,12 +411,40 @@ __device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const EpiCoord
   });
 }
 
+// A-operand fragment of a diagonal matrix v I for one 16-k half (kk) of a
+// 32-k step whose k range equals the 32 output rows of an accumulator block:
+// lane (m = l & 31, h = l >> 5) supplies row m at k = 16 kk + 8 h + e, so
+// only the element with 16 kk + 8 h + e == m is nonzero.
+__device__ inline bf16x8 diag_frag(float v, int lane, int kk) {
+  const int e = (lane & 31) - 16 * kk - 8 * (lane >> 5);
+  bf16x8 f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) f[x] = bf16(x == e ? v : 0.f);
+  return f;
+}
+
+// Two ds_read_b64_tr_b16 four rows apart: from a [k][column] LDS stage, lane
+// l receives 8 consecutive k of one column, the B-operand layout of
+// v_mfma_f32_32x32x16_bf16. Within each group of 16 lanes, lane s points at
+// row s >> 2 and columns 4 (s & 3) .. + 3 of a 4 x 16 block; the transposing
+// read hands lane s column s of that block, rows 0..3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+__device__ inline bf16x8 tr_frag(const char *p) {
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p + 4 * 512));
+  const s16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
 template <int PHASE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // the wave index goes through readfirstlane so that the compiler sees it
+  // (and the K-loop bounds derived from it) as uniform
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 1, wn = wv & 1;
   const int tile = args.remap ? xcd_remap(blockIdx.x, args.total_tiles) : int(blockIdx.x);
   const TileInfo ti = decode_tile(args, tile, PHASE != kBX);
@@ -420,6 +453,9 @@ void gemm_bf16_kernel(const GemmArgs args) {
   const int mp = S.mp, np = S.np;
   const int i0 = ti.I * kBM, j0 = ti.J * kBM;
 
+  // P: rows i of the left operand, K-contiguous. Q: rows j, K-contiguous
+  // (Gram, A*A), or rows k of X (B X; B is symmetric, so its rows i serve
+  // as P).
   const bf16 *P, *Q, *P2, *Q2;
   int64_t ld;
   int K;
@@ -434,26 +470,54 @@ void gemm_bf16_kernel(const GemmArgs args) {
     K = args.aa_plain ? mp : 3 * mp;
   } else {
     P = P2 = reinterpret_cast<const bf16 *>(blk + S.off_b);
-    Q = Q2 = reinterpret_cast<const bf16 *>(blk + S.off_xt[args.src]);
+    Q = Q2 = reinterpret_cast<const bf16 *>(blk + S.off_xa[args.src]);
     ld = mp;
     K = mp;
   }
 
-  // Global -> LDS: each wave issues 4 loads per operand per K step; load q of
-  // wave w fills rows (4 w + q) * 16 .. + 15 (1 KiB). Lane L carries row
-  // base + L / 4 and the logical k chunk that belongs in physical chunk L % 4.
+  // Global -> LDS: each wave issues 4 loads per operand per K step.
+  // K-contiguous operand: load q of wave w fills rows (4 w + q) * 16 .. + 15
+  // (64-byte rows, 1 KiB); lane L carries row base + L / 4 and the logical k
+  // chunk that belongs in physical chunk L % 4.
+  // X rows (B X): the stage is 32 rows k x 512 bytes; load q of wave w fills
+  // rows 2 (4 w + q) and + 1; lane L carries physical 16-byte chunk L % 32 of
+  // its row, whose 64-byte unit is the logical unit XOR (k & 3).
   const int lrow0 = lane >> 2;
   const int lphys = lane & 3;
-  int64_t goff[4];   // element offset of this lane's 16 bytes, per q (k0 = 0)
-  int loff[4];       // LDS byte offset of the 1 KiB block, per q (wave-uniform)
+  int64_t goff[4], qoff[4];
+  int loff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = (wv * 4 + q) * 16 + lrow0;
     const int lc = lphys ^ ((row >> 2) & 3);
     goff[q] = int64_t(row) * ld + lc * 8;
     loff[q] = (wv * 4 + q) * 1024;
+    if (PHASE == kBX) {
+      const int kr = (wv * 4 + q) * 2 + (lane >> 5), pc = lane & 31;
+      qoff[q] = int64_t(kr) * np + (((pc >> 2) ^ (kr & 3)) << 5) + (pc & 3) * 8;
+    } else {
+      qoff[q] = goff[q];
+    }
   }
-  const int64_t prow0 = int64_t(i0) * ld, qrow0 = int64_t(j0) * ld;
+  const int64_t prow0 = int64_t(i0) * ld;
+  const int64_t qrow0 = PHASE == kBX ? int64_t(j0) : int64_t(j0) * ld;
+  const int64_t qkmul = PHASE == kBX ? int64_t(np) : 1;
+  // B X runs its K loop from the tile's own diagonal block (k = i0) around
+  // to i0 - 1: the row tiles that share a column panel then read different
+  // rows of X at any moment instead of the same 32 rows, which spreads the
+  // concurrent X reads over the memory channels. (It also puts the K steps
+  // whose k range equals a block row of the output at iterations
+  // 4 wm + bi, the same in every tile.)
+  const int krot = PHASE == kBX ? i0 : 0;
+
+  // B X: a + diag(B) for the row this lane supplies in each block row
+  // (loaded ahead of the operand ring, so the first wait covers it)
+  float coef_v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (PHASE == kBX) {
+    const float *bdiag = reinterpret_cast<const float *>(blk + S.off_bdiag) + i0 + wm * 128 + (lane & 31);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) coef_v[bi] = args.a + bdiag[bi * 32];
+  }
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -470,12 +534,21 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // multiples of 32 rows)
   const int fa = (wm * 128 + fr) * 64, fb = (wn * 128 + fr) * 64;
   const int fx = (fr >> 2) & 3;
+  // B X: transposing reads of the X stage. Lane s of each 16-lane group
+  // reads row 8 h + (s >> 2) (+ 16 kk + 4 t) at column 4 (s & 3) + 16 g of
+  // block bj; rows k & 3 = 0..3 of one read land in 4 distinct 64-byte units.
+  const int trow = (lane & 15) >> 2;
+  const int qtr = (8 * fh + trow) * 512 + (4 * (lane & 3) + 16 * ((lane >> 4) & 1)) * 2;
+  int qun[4];
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) qun[bj] = ((4 * wn + bj) ^ trow) << 6;
 
   // issue the loads of K step ks_ into its stage (for A*A, K runs over three
   // segments of length mp: hi*hi, hi*lo, lo*hi)
 #define MUON_GLOAD(ks_)                                                              \
   do {                                                                               \
     int k0_ = (ks_) * kBK;                                                           \
+    if (PHASE == kBX) k0_ = k0_ + krot < K ? k0_ + krot : k0_ + krot - K;            \
     const bf16 *pa_ = P, *qa_ = Q;                                                   \
     if (PHASE == kAA) {                                                              \
       const int sgm_ = k0_ / mp;                                                     \
@@ -483,25 +556,31 @@ void gemm_bf16_kernel(const GemmArgs args) {
       pa_ = sgm_ == 2 ? P2 : P;                                                      \
       qa_ = sgm_ == 1 ? Q2 : Q;                                                      \
     }                                                                                \
-    char *st_ = smem + ((ks_) & (kStages - 1)) * kStageBytes;                        \
+    const int64_t qk_ = int64_t(k0_) * qkmul;                                        \
+    char *st_ = smem + ((ks_) % kStages) * kStageBytes;                              \
     _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
       __builtin_amdgcn_global_load_lds(                                              \
           (const __attribute__((address_space(1))) void *)(pa_ + prow0 + goff[q] + k0_), \
           (__attribute__((address_space(3))) void *)(st_ + loff[q]), 16, 0, 0);      \
       __builtin_amdgcn_global_load_lds(                                              \
-          (const __attribute__((address_space(1))) void *)(qa_ + qrow0 + goff[q] + k0_), \
+          (const __attribute__((address_space(1))) void *)(qa_ + qrow0 + qoff[q] + qk_), \
           (__attribute__((address_space(3))) void *)(st_ + kOpBytes + loff[q]), 16, 0, 0); \
     }                                                                                \
   } while (0)
 #define MUON_FRAGS(buf_, ks_, kk_)                                                   \
   do {                                                                               \
-    const char *As_ = smem + ((ks_) & (kStages - 1)) * kStageBytes;                  \
+    const char *As_ = smem + ((ks_) % kStages) * kStageBytes;                        \
     const char *Bs_ = As_ + kOpBytes;                                                \
     const int ch_ = (((kk_) * 2 + fh) ^ fx) << 4;                                    \
     _Pragma("unroll") for (int bi = 0; bi < 4; ++bi)                                 \
       af[buf_][bi] = *reinterpret_cast<const bf16x8 *>(As_ + fa + bi * 2048 + ch_);  \
-    _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                                 \
-      bq[buf_][bj] = *reinterpret_cast<const bf16x8 *>(Bs_ + fb + bj * 2048 + ch_);  \
+    if (PHASE == kBX) {                                                              \
+      _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                               \
+        bq[buf_][bj] = tr_frag(Bs_ + (kk_) * 16 * 512 + qtr + qun[bj]);              \
+    } else {                                                                         \
+      _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                               \
+        bq[buf_][bj] = *reinterpret_cast<const bf16x8 *>(Bs_ + fb + bj * 2048 + ch_); \
+    }                                                                                \
   } while (0)
 #define MUON_MFMA(buf_)                                                              \
   do {                                                                               \
@@ -512,47 +591,112 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
   // [15:14], expcnt[6:4] and lgkmcnt[11:8] left at their maxima)
 #define MUON_WAIT_VM(n_) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0F70)
+  // One K step. Step ks + 1 landed for this wave (ks + 2, ks + 3 in flight);
+  // after the barrier it has landed for every wave, and every wave has
+  // consumed step ks - 1. A bare s_barrier: the fragment reads still in
+  // flight here target step ks, never the stage the next loads overwrite.
+#define MUON_STEP_CORE(ks_, CAP0_, CAP1_)                                            \
+  do {                                                                               \
+    MUON_WAIT_VM(16);                                                                \
+    __builtin_amdgcn_s_barrier();                                                    \
+    MUON_GLOAD((ks_) + 4 < kl ? (ks_) + 4 : kl);                                     \
+    MUON_FRAGS(1, ks_, 1);                                                           \
+    MUON_MFMA(0);                                                                    \
+    CAP0_;                                                                           \
+    MUON_FRAGS(0, (ks_) + 1, 0); /* stage of ks + 1 (re-reads the last stage at the end) */ \
+    MUON_MFMA(1);                                                                    \
+    CAP1_;                                                                           \
+  } while (0)
+#define MUON_STEP(ks_)                                                               \
+  do {                                                                               \
+    MUON_STEP_CORE(ks_, (void)0, (void)0);                                           \
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0); /* global->LDS loads first */ \
+    _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                 \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                             \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
+    }                                                                                \
+  } while (0)
+  // The additive terms of B = b A + c A A and X' = (a + diag B) X + B' X
+  // enter as products with a diagonal matrix: in the K step whose 32 k are
+  // the 32 output rows of block row bi_, the Q fragments hold exactly the
+  // A (or X) values of those outputs, and D Q adds D_mm Q[m][:] to row m.
+  // The diagonal goes in as bf16 hi + lo parts (hi only for the small lo
+  // half of A).
+#define MUON_CAPTURE(buf_, bi_, dh_, dl_, lo_)                                       \
+  do {                                                                               \
+    _Pragma("unroll") for (int bj = 0; bj < 4; ++bj) {                               \
+      acc[bi_][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dh_[buf_], bq[buf_][bj], acc[bi_][bj], 0, 0, 0); \
+      if (lo_) acc[bi_][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dl_[buf_], bq[buf_][bj], acc[bi_][bj], 0, 0, 0); \
+    }                                                                                \
+  } while (0)
 
-  // Steps past the end re-load the last step into a stage nobody reads
-  // again; this keeps 8 loads per wave per step, so the vmcnt arithmetic
-  // below is the same in every iteration.
+  // Steps past the end re-load the last step into its own stage (the same
+  // bytes again); this keeps 8 loads per wave per step, so the vmcnt
+  // arithmetic below is the same in every iteration.
   const int kl = nk - 1;
   bf16x8 af[2][4], bq[2][4];
   MUON_GLOAD(0);
   MUON_GLOAD(1 < kl ? 1 : kl);
   MUON_GLOAD(2 < kl ? 2 : kl);
-  MUON_WAIT_VM(16);  // step 0 landed (steps 1, 2 in flight)
+  MUON_GLOAD(3 < kl ? 3 : kl);
+  MUON_WAIT_VM(24);  // step 0 landed (steps 1..3 in flight)
   __syncthreads();
   MUON_FRAGS(0, 0, 0);
-  for (int ks = 0; ks < nk; ++ks) {
-    // Step ks + 1 landed for this wave (ks + 2 in flight); after the barrier
-    // it has landed for every wave, and every wave has consumed step ks - 1.
-    // A bare s_barrier: the fragment reads still in flight here target step
-    // ks (stage ks & 3), never the stage the next loads overwrite.
-    MUON_WAIT_VM(8);
-    __builtin_amdgcn_s_barrier();
-    MUON_GLOAD(ks + 3 < kl ? ks + 3 : kl);
-    MUON_FRAGS(1, ks, 1);
-    MUON_MFMA(0);
-    MUON_FRAGS(0, ks + 1, 0);  // stage of ks + 1 (re-reads the last stage at the end)
-    MUON_MFMA(1);
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // global->LDS loads first
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  int ks = 0;
+  if (PHASE == kGram) {
+    for (; ks < nk; ++ks) MUON_STEP(ks);
+  } else {
+    if (PHASE == kAA) {
+      // the K step whose k range equals this wave's first output rows
+      const int c0 = ti.I * (kBM / kBK) + wm * (128 / kBK);
+      const float r = args.r, rh = float(bf16(r));
+      const bf16x8 dh[2] = {diag_frag(rh, lane, 0), diag_frag(rh, lane, 1)};
+      const bf16x8 dl[2] = {diag_frag(r - rh, lane, 0), diag_frag(r - rh, lane, 1)};
+#define MUON_CAP_STEPS(lo_)                                                          \
+      do {                                                                           \
+        MUON_STEP_CORE(ks, MUON_CAPTURE(0, 0, dh, dl, lo_), MUON_CAPTURE(1, 0, dh, dl, lo_)); ++ks; \
+        MUON_STEP_CORE(ks, MUON_CAPTURE(0, 1, dh, dl, lo_), MUON_CAPTURE(1, 1, dh, dl, lo_)); ++ks; \
+        MUON_STEP_CORE(ks, MUON_CAPTURE(0, 2, dh, dl, lo_), MUON_CAPTURE(1, 2, dh, dl, lo_)); ++ks; \
+        MUON_STEP_CORE(ks, MUON_CAPTURE(0, 3, dh, dl, lo_), MUON_CAPTURE(1, 3, dh, dl, lo_)); ++ks; \
+      } while (0)
+      // segment hi*hi: r A_hi (+ its bf16 rounding remainder)
+      for (; ks < c0; ++ks) MUON_STEP(ks);
+      MUON_CAP_STEPS(true);
+      if (!args.aa_plain) {
+        // segment hi*lo: its Q fragments hold A_lo, which is symmetric too
+        const int c1 = mp / kBK + c0;
+        for (; ks < c1; ++ks) MUON_STEP(ks);
+        MUON_CAP_STEPS(false);
+      }
+#undef MUON_CAP_STEPS
+    } else {
+      // K step c0 + bi is loop iteration 4 wm + bi (rotated K loop)
+      const int cb = wm * (128 / kBK);
+      for (; ks < cb; ++ks) MUON_STEP(ks);
+#define MUON_CAP_STEP(bi_)                                                           \
+      do {                                                                           \
+        const float cv = coef_v[bi_], ch = float(bf16(cv));                          \
+        const bf16x8 dh[2] = {diag_frag(ch, lane, 0), diag_frag(ch, lane, 1)};       \
+        const bf16x8 dl[2] = {diag_frag(cv - ch, lane, 0), diag_frag(cv - ch, lane, 1)}; \
+        MUON_STEP_CORE(ks, MUON_CAPTURE(0, bi_, dh, dl, true), MUON_CAPTURE(1, bi_, dh, dl, true)); \
+        ++ks;                                                                        \
+      } while (0)
+      MUON_CAP_STEP(0);
+      MUON_CAP_STEP(1);
+      MUON_CAP_STEP(2);
+      MUON_CAP_STEP(3);
+#undef MUON_CAP_STEP
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    for (; ks < nk; ++ks) MUON_STEP(ks);
   }
   MUON_WAIT_VM(0);  // no load may still target LDS when the workgroup ends
 #undef MUON_GLOAD
 #undef MUON_FRAGS
 #undef MUON_MFMA
 #undef MUON_WAIT_VM
+#undef MUON_STEP_CORE
+#undef MUON_STEP
+#undef MUON_CAPTURE
 
   // ---------------- epilogues ----------------
   __syncthreads();  // every wave is done with the LDS ring
@@ -572,8 +716,11 @@ void gemm_bf16_kernel(const GemmArgs args) {
         a[r] = __uint_as_float(pack_bf16(x, x - float(bf16(x))));
       }
     });
+    // (the lo half is not needed when A*A runs on bf16(A) alone)
+    const int halves = args.aa_plain ? 1 : 2;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {  // 0: hi (bits 16..31), 1: lo
+      if (half >= halves) break;
       bf16 *dst = reinterpret_cast<bf16 *>(blk + (half ? S.off_alo : S.off_ahi));
       const int shift = half ? 0 : 16;
       fill_tile<true>(smem, acc, ec, shift);
@@ -590,28 +737,11 @@ void gemm_bf16_kernel(const GemmArgs args) {
       lds_barrier();
     }
   } else if (PHASE == kAA) {
-    // B = b A + c A A. A's tile comes in from the mirror position (J, I),
-    // whose rows are the columns of tile (I, J): A[i][j] = A[j][i].
-    const bf16 *Ah = reinterpret_cast<const bf16 *>(blk + S.off_ahi);
-    const bf16 *Al = reinterpret_cast<const bf16 *>(blk + S.off_alo);
+    // B = c (A A + r A), r = b / c added in the K loop
     for_blocks(acc, [&](f32x16 &a, int, int) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] *= args.c;
     });
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      tile_load(smem, half ? Al : Ah, mp, j0, i0, tid);
-      lds_barrier();
-      for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const bf16x4 h4 = get_trans(smem, ec, bi, bj, r4);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) a[r4 * 4 + q] = fmaf(args.b, float(h4[q]), a[r4 * 4 + q]);
-        }
-      });
-      lds_barrier();
-    }
     // The diagonal of B stays in float32 (bdiag); B stores it as zero. Only
     // blocks (bb, bb) of the waves with wm == wn in a diagonal tile hold
     // diagonal elements: row 8 r4 + 4 fh + q equals column fr for the lanes
@@ -647,44 +777,24 @@ void gemm_bf16_kernel(const GemmArgs args) {
       tile_store(smem, Bm, mp, i0, j0, tid);  // tile (I, J)
     }
   } else {
-    // X' = s'' ((a + B_ii) X + B_offdiag X): X's tile comes in from X^T
-    // (rows j), the result leaves as X'^T (rows j) and X' (rows i)
+    // X' = s'' ((a + B_ii) X + B_offdiag X), the first term added in the K loop
     const float sx = args.first ? scale_p[0] : 1.f;
-    const float *bdiag = reinterpret_cast<const float *>(blk + S.off_bdiag);
-    const bf16 *Xt = reinterpret_cast<const bf16 *>(blk + S.off_xt[args.src]);
-    bf16 *Ya = reinterpret_cast<bf16 *>(blk + S.off_xa[args.src ^ 1]);
-    bf16 *Yt = reinterpret_cast<bf16 *>(blk + S.off_xt[args.src ^ 1]);
-    tile_load(smem, Xt, mp, j0, i0, tid);
-    lds_barrier();
-    for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+    bf16 *Y = reinterpret_cast<bf16 *>(blk + S.off_xa[args.src ^ 1]);
+    for_blocks(acc, [&](f32x16 &a, int, int) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int ti_ = ec.ib + bi * 32 + r4 * 8;
-        const bf16x4 x4 = get_trans(smem, ec, bi, bj, r4);
-        const float4 d4 = *reinterpret_cast<const float4 *>(bdiag + i0 + ti_);
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float o = sx * fmaf(args.a + dd[q], float(x4[q]), a[r4 * 4 + q]);
-          a[r4 * 4 + q] = __uint_as_float(pack_bf16(0.f, o));
-        }
-      }
+      for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, sx * a[r]));
     });
-    lds_barrier();  // every lane has read its X values before the tile is overwritten
-    fill_tile<true>(smem, acc, ec, 0);
-    lds_barrier();
-    tile_store(smem, Yt, mp, j0, i0, tid);  // X'^T rows j
-    lds_barrier();
     fill_tile<false>(smem, acc, ec, 0);
     lds_barrier();
-    tile_store(smem, Ya, np, i0, j0, tid);  // X' rows i
+    tile_store(smem, Y, np, i0, j0, tid);
   }
 }
 
 // ---------------------------------------------------------------------------
 // float32 kernel (VALU FMA): 64x64 output tile, K step 16, 256 threads, each
-// thread 4x4 outputs strided by 16. Same phases and epilogues as above, with
-// float32 storage everywhere (A in the hi slot, no lo half).
+// thread 4x4 outputs strided by 16. Same phases as above with float32
+// storage everywhere (A in the hi slot, no lo half, B with its diagonal);
+// the terms b A and a X come from memory in the epilogue.
 // ---------------------------------------------------------------------------
 
 template <int PHASE>
@@ -707,25 +817,34 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs args) {
     P = Q = reinterpret_cast<const float *>(blk + S.off_ahi);
     ld = mp;
     K = mp;
-  } else {
+  } else {  // B is symmetric: its rows i serve as P; Q is X, read by rows k
     P = reinterpret_cast<const float *>(blk + S.off_b);
-    Q = reinterpret_cast<const float *>(blk + S.off_xt[args.src]);
+    Q = reinterpret_cast<const float *>(blk + S.off_xa[args.src]);
     ld = mp;
     K = mp;
   }
   float acc[4][4] = {};
   const int lr = tid >> 2, lk = (tid & 3) * 4;
+  const int kr = tid >> 4, kc = (tid & 15) * 4;
   for (int k0 = 0; k0 < K; k0 += 16) {
     const float4 pa = *reinterpret_cast<const float4 *>(P + int64_t(i0 + lr) * ld + k0 + lk);
-    const float4 qa = *reinterpret_cast<const float4 *>(Q + int64_t(j0 + lr) * ld + k0 + lk);
     As[lk + 0][lr] = pa.x;
     As[lk + 1][lr] = pa.y;
     As[lk + 2][lr] = pa.z;
     As[lk + 3][lr] = pa.w;
-    Bs[lk + 0][lr] = qa.x;
-    Bs[lk + 1][lr] = qa.y;
-    Bs[lk + 2][lr] = qa.z;
-    Bs[lk + 3][lr] = qa.w;
+    if (PHASE == kBX) {
+      const float4 qa = *reinterpret_cast<const float4 *>(Q + int64_t(k0 + kr) * np + j0 + kc);
+      Bs[kr][kc + 0] = qa.x;
+      Bs[kr][kc + 1] = qa.y;
+      Bs[kr][kc + 2] = qa.z;
+      Bs[kr][kc + 3] = qa.w;
+    } else {
+      const float4 qa = *reinterpret_cast<const float4 *>(Q + int64_t(j0 + lr) * ld + k0 + lk);
+      Bs[lk + 0][lr] = qa.x;
+      Bs[lk + 1][lr] = qa.y;
+      Bs[lk + 2][lr] = qa.z;
+      Bs[lk + 3][lr] = qa.w;
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -763,15 +882,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs args) {
     const float sx = args.first ? reinterpret_cast<const float *>(blk + S.off_scale)[0] : 1.f;
     const float *X = reinterpret_cast<const float *>(blk + S.off_xa[args.src]);
     float *Ya = reinterpret_cast<float *>(blk + S.off_xa[args.src ^ 1]);
-    float *Yt = reinterpret_cast<float *>(blk + S.off_xt[args.src ^ 1]);
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int i = i0 + ty + 16 * x, j = j0 + tx + 16 * y;
-        const float o = sx * fmaf(args.a, X[int64_t(i) * np + j], acc[x][y]);
-        Ya[int64_t(i) * np + j] = o;
-        Yt[int64_t(j) * mp + i] = o;
+        Ya[int64_t(i) * np + j] = sx * fmaf(args.a, X[int64_t(i) * np + j], acc[x][y]);
       }
   }
 }

@@ -39,8 +39,6 @@ Layout view_layout(int64_t mp, int64_t np, bool bf16) {
   for (int p = 0; p < 2; ++p) {
     L.xa[p] = off;
     off = align_up(off + mn, 256);
-    L.xt[p] = off;
-    off = align_up(off + mn, 256);
   }
   L.ahi = off;
   off = align_up(off + mm, 256);
@@ -60,7 +58,7 @@ Layout view_layout(int64_t mp, int64_t np, bool bf16) {
 }
 
 bool validate_mode(uint32_t mode, Error *err) {
-  const uint32_t known = MUON_NS_BLOCKWISE | MUON_PACK_COST | MUON_AA_PLAIN;
+  const uint32_t known = MUON_NS_BLOCKWISE | MUON_PACK_COST | MUON_AA_SPLIT;
   if (mode & ~known) return err->set(MUON_ERR_INVALID_ARG, fmt("unknown mode bits 0x%llx", mode & ~known));
   return true;
 }
@@ -261,7 +259,7 @@ std::string plan_json(const Plan &p) {
         << ",\"base\":" << sg.base << ",\"stride\":" << sg.stride << ",\"tiles_syrk\":" << sg.tiles_syrk
         << ",\"tiles_gemm\":" << sg.tiles_gemm;
       const Layout L = view_layout(sg.mp, sg.np, p.bf16);
-      o << ",\"layout\":{\"xa\":[" << L.xa[0] << "," << L.xa[1] << "],\"xt\":[" << L.xt[0] << "," << L.xt[1]
+      o << ",\"layout\":{\"xa\":[" << L.xa[0] << "," << L.xa[1]
         << "],\"ahi\":" << L.ahi << ",\"alo\":" << L.alo << ",\"b\":" << L.b << ",\"bdiag\":" << L.bdiag
         << ",\"partials\":" << L.partials
         << ",\"scale\":" << L.scale << ",\"total\":" << L.total << "}}";

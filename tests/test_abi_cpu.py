@@ -70,6 +70,13 @@ def test_ns_validation_codes(lib):
     assert "workspace" in mu.muon_last_error()
     nan = (ctypes.c_float * 3)(float("nan"), 0, 0)
     assert lib.muon_ns_batched(mu.mats([desc(4, 8)]), 1, 5, nan, 0) == mu.MUON_ERR_INVALID_ARG
+    # B is formed as c (A A + (b / c) A): c == 0 (a cubic iteration) and an
+    # overflowing b / c are rejected before anything else
+    for bad in [(1.5, -0.5, 0.0), (3.0, -3e38, 1e-3)]:
+        cf = (ctypes.c_float * 3)(*bad)
+        assert lib.muon_ns_batched(mu.mats([desc(4, 8)]), 1, 5, cf, 0) == mu.MUON_ERR_INVALID_ARG
+        assert "c != 0" in mu.muon_last_error()
+        assert lib.muon_set_step_options(5, cf, 1e-7, 0) == mu.MUON_ERR_INVALID_ARG
 
 
 def test_alias_exact_for_interleaved_views(lib):
@@ -204,8 +211,7 @@ def test_plan_blockwise_expansion():
 def test_plan_layout_disjoint():
     p = mu.muon_plan_info(shapes_descs([(300, 520)]))
     L = p["chunks"][0]["segments"][0]["layout"]
-    spans = sorted([L["xa"][0], L["xa"][1], L["xt"][0], L["xt"][1], L["ahi"], L["alo"], L["b"],
-                    L["partials"], L["scale"]])
+    spans = sorted([L["xa"][0], L["xa"][1], L["ahi"], L["alo"], L["b"], L["partials"], L["scale"]])
     assert spans == sorted(set(spans)) and all(x % 256 == 0 for x in spans)
     assert L["total"] > L["scale"]
 

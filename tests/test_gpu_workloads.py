@@ -29,17 +29,18 @@ LR32 = float(np.float32(0.02))
 BETA32 = float(np.float32(0.95))
 
 
-def run_step_checks(gpu_lib, name, sample):
+def run_step_checks(gpu_lib, name, sample, aa_mode=None):
     import muon_newton_schulz_03_amd as mu
     from muon_newton_schulz_03_amd.workloads import WORKLOADS, make_inputs
     wl = WORKLOADS[name]
     W, G, M = make_inputs(wl)
     torch.cuda.synchronize()
-    print(f"{name}: {len(W)} matrices, sample {sample}", flush=True)
+    aa = mu.MUON_AA_PLAIN if aa_mode is None else aa_mode
+    print(f"{name}: {len(W)} matrices, sample {sample}, A*A mode {aa:#x}", flush=True)
     G0 = {i: np64(G[i]) for i in sample}
     M0 = {i: np64(M[i]) for i in sample}
     W0 = {i: np64(W[i]) for i in sample}
-    mode = mu.MUON_PACK_COST | (mu.MUON_NS_BLOCKWISE if wl.col_blocks > 1 else 0)
+    mode = mu.MUON_PACK_COST | aa | (mu.MUON_NS_BLOCKWISE if wl.col_blocks > 1 else 0)
     cb = [wl.col_blocks] * len(W)
     Mc = [t.clone() for t in M]
     Wz = [torch.zeros_like(t) for t in W]
@@ -81,6 +82,16 @@ def test_kimi_moe_layer_full(gpu_lib):
 
 def test_kimi_dense_blockwise_full(gpu_lib):
     run_step_checks(gpu_lib, "kimi_dense_blockwise", [0])
+
+
+@pytest.mark.parametrize("name", ["qwen3_block", "kimi_moe_layer", "kimi_dense_blockwise"])
+def test_split_aa_full(gpu_lib, name):
+    """A*A and b A from A as bf16 hi + lo, at the full sizes."""
+    import muon_newton_schulz_03_amd as mu
+    from muon_newton_schulz_03_amd.workloads import WORKLOADS, sample_indices
+    n = len(WORKLOADS[name].shapes)
+    sample = sorted(set(sample_indices(n, 4, 7) + [0, n - 1]))
+    run_step_checks(gpu_lib, name, sample, aa_mode=mu.MUON_AA_SPLIT)
 
 
 @pytest.mark.parametrize("index", [0, 2])

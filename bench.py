@@ -221,7 +221,7 @@ def main():
         out["roofline"] = {
             "bound": "mfma",
             "kernel": {"gram": "gemm_bf16_kernel<0> (SYRK Gram)", "aa": "gemm_bf16_kernel<1> (SYRK A*A + poly)",
-                       "bx": "gemm_bf16_kernel<2> (GEMM B*X + axpy)"}[dom],
+                       "bx": "gemm_bf16_kernel<2> (GEMM B*X + (a + diag B) X)"}[dom],
             "achieved": round(ach, 2),
             "peak": round(PEAK_BF16_TFLOPS, 1),
             "unit": "TFLOP/s",

@@ -85,6 +85,15 @@ struct Sources {
   const muon_mat *W = nullptr, *G = nullptr, *M = nullptr;  // muon_step
 };
 
+// Workgroups of a persistent launch: one per compute unit of the current
+// device, rounded down to a multiple of the 8 XCDs (0 if unknown).
+int persistent_slots() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return (cus / 8) * 8;
+}
+
 muon_status hip_fail(hipError_t e, const char *what) {
   return fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -97,6 +106,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
   const bool bf16 = plan.bf16;
   const int iters = plan.iters;
   const int fin = iters & 1;
+  const int slots = bf16 ? persistent_slots() : 0;
 
   for (const Chunk &ch : plan.chunks) {
     // per-view workspace blocks, in plan order
@@ -231,7 +241,11 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       e = timed(kTAA, st, [&] { return launch_gemm(ga, kAA, bf16, st); });
       if (e != hipSuccess) return hip_fail(e, "A*A launch");
       set_tiles(false);
+      // B X (short K loop): persistent workgroups, so that a tile's epilogue
+      // stores overlap the next tile's first operand loads
+      ga.persistent = (slots > 0 && ga.total_tiles > slots) ? slots : 0;
       e = timed(kTBX, st, [&] { return launch_gemm(ga, kBX, bf16, st); });
+      ga.persistent = 0;
       if (e != hipSuccess) return hip_fail(e, "B*X launch");
     }
     s = elem_pass(false);

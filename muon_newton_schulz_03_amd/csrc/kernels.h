@@ -77,6 +77,8 @@ struct GemmArgs {
   int32_t first;    // first iteration: apply the normalization scale
   int32_t aa_plain; // A*A and b A from bf16(A) only (no lo half of A)
   int32_t remap;    // XCD-aware tile order
+  int32_t persistent; // > 0: grid of this many workgroups (a multiple of 8),
+                      // each looping over tiles of its XCD's range
   float a, b, c;
   float r;          // b / c: the A*A kernel adds r A inside its K loop, then scales by c
   float eps;

@@ -397,6 +397,21 @@ __device__ inline void put_trans(char *smem, const EpiCoord &e, int bi, int bj, 
   const int tj = e.jb + bj * 32, ti = e.ib + bi * 32 + r4 * 8;
   *reinterpret_cast<u32x2 *>(smem + tile_off(tj, ti)) = v;
 }
+// Stores the packed accumulators (bits [0, 16)) of a 256 x 256 tile to a
+// row-major matrix from the registers: the same quad transpose as
+// put_direct, then one 8-byte store of 4 consecutive columns per lane.
+__device__ inline void store_direct(bf16 *dst, int64_t pitch, f32x16 (&acc)[4][4], const EpiCoord &e) {
+  for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int p = e.jb & 3;
+      const u32x2 t = quad_transpose(unpack4(a, r4, 0), p);
+      const int ti = e.ib + bi * 32 + r4 * 8 + p, tj = e.jb - p + bj * 32;
+      *reinterpret_cast<u32x2 *>(dst + int64_t(ti) * pitch + tj) = t;
+    }
+  });
+}
+
 template <bool TRANS>
 __device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const EpiCoord &e, int shift) {
   for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
@@ -444,10 +459,34 @@ void gemm_bf16_kernel(const GemmArgs args) {
 
   // the wave index goes through readfirstlane so that the compiler sees it
   // (and the K-loop bounds derived from it) as uniform
-  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
   const int wm = wv >> 1, wn = wv & 1;
-  const int tile = args.remap ? xcd_remap(blockIdx.x, args.total_tiles) : int(blockIdx.x);
-  const TileInfo ti = decode_tile(args, tile, PHASE != kBX);
+
+  // Tiles of this workgroup: one (the grid covers every tile), or, in a
+  // persistent launch (8 S workgroups, S per XCD), the tiles begin + slot,
+  // begin + slot + S, ... of its XCD's contiguous range, so that the 8 XCDs
+  // each work through their own contiguous part of the tile order.
+  int t_cur, t_end, t_step;
+  if (args.persistent) {
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int q = args.total_tiles >> 3, r = args.total_tiles & 7;
+    const int begin = x * q + min(x, r);
+    t_cur = begin + slot;
+    t_end = begin + q + (x < r ? 1 : 0);
+    t_step = int(gridDim.x) >> 3;
+  } else {
+    t_cur = args.remap ? xcd_remap(blockIdx.x, args.total_tiles) : int(blockIdx.x);
+    t_end = t_cur + 1;
+    t_step = 1;
+  }
+  for (; t_cur < t_end; t_cur += t_step) {
+  // The thread index passes through an empty asm each tile, so the address
+  // arithmetic derived from it is recomputed per tile instead of being
+  // hoisted out of the tile loop (and spilled).
+  int tid = int(threadIdx.x);
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const TileInfo ti = decode_tile(args, t_cur, PHASE != kBX);
   const GemmSeg &S = args.seg[ti.seg];
   char *blk = S.base + int64_t(ti.view) * S.stride;
   const int mp = S.mp, np = S.np;
@@ -639,8 +678,8 @@ void gemm_bf16_kernel(const GemmArgs args) {
   MUON_GLOAD(1 < kl ? 1 : kl);
   MUON_GLOAD(2 < kl ? 2 : kl);
   MUON_GLOAD(3 < kl ? 3 : kl);
-  MUON_WAIT_VM(24);  // step 0 landed (steps 1..3 in flight)
-  __syncthreads();
+  MUON_WAIT_VM(24);  // step 0 landed (steps 1..3 in flight; earlier stores done)
+  __builtin_amdgcn_s_barrier();
   MUON_FRAGS(0, 0, 0);
   int ks = 0;
   if (PHASE == kGram) {
@@ -689,7 +728,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
     }
     for (; ks < nk; ++ks) MUON_STEP(ks);
   }
-  MUON_WAIT_VM(0);  // no load may still target LDS when the workgroup ends
+  MUON_WAIT_VM(0);  // no load may still target LDS past the K loop
 #undef MUON_GLOAD
 #undef MUON_FRAGS
 #undef MUON_MFMA
@@ -699,7 +738,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #undef MUON_CAPTURE
 
   // ---------------- epilogues ----------------
-  __syncthreads();  // every wave is done with the LDS ring
+  if (PHASE != kBX) __syncthreads();  // every wave is done with the LDS ring
   const EpiCoord ec{wm * 128 + fh * 4, wn * 128 + fr};
   const bool diag = (PHASE != kBX) && ti.I == ti.J;
   float *scale_p = reinterpret_cast<float *>(blk + S.off_scale);
@@ -718,9 +757,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
     });
     // (the lo half is not needed when A*A runs on bf16(A) alone)
     const int halves = args.aa_plain ? 1 : 2;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {  // 0: hi (bits 16..31), 1: lo
-      if (half >= halves) break;
+    for (int half = 0; half < halves; ++half) {  // 0: hi (bits 16..31), 1: lo
       bf16 *dst = reinterpret_cast<bf16 *>(blk + (half ? S.off_alo : S.off_ahi));
       const int shift = half ? 0 : 16;
       fill_tile<true>(smem, acc, ec, shift);
@@ -777,17 +814,19 @@ void gemm_bf16_kernel(const GemmArgs args) {
       tile_store(smem, Bm, mp, i0, j0, tid);  // tile (I, J)
     }
   } else {
-    // X' = s'' ((a + B_ii) X + B_offdiag X), the first term added in the K loop
+    // X' = s'' ((a + B_ii) X + B_offdiag X), the first term added in the K
+    // loop; stored straight from the registers (no LDS), so the loads of the
+    // next tile of a persistent launch can start right behind the stores
     const float sx = args.first ? scale_p[0] : 1.f;
     bf16 *Y = reinterpret_cast<bf16 *>(blk + S.off_xa[args.src ^ 1]);
     for_blocks(acc, [&](f32x16 &a, int, int) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, sx * a[r]));
     });
-    fill_tile<false>(smem, acc, ec, 0);
-    lds_barrier();
-    tile_store(smem, Y, np, i0, j0, tid);
+    store_direct(Y + int64_t(i0) * np + j0, np, acc, ec);
+    lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
   }
+  }  // tiles of this workgroup
 }
 
 // ---------------------------------------------------------------------------
@@ -911,7 +950,7 @@ hipError_t launch_norm_finalize(const GemmArgs &a, int views, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs &a, int phase, bool bf16, hipStream_t s) {
   if (a.total_tiles <= 0) return hipSuccess;
-  const dim3 grid(a.total_tiles), block(256);
+  const dim3 grid(a.persistent ? a.persistent : a.total_tiles), block(256);
   if (bf16) {
     switch (phase) {
       case kGram: hipLaunchKernelGGL(gemm_bf16_kernel<kGram>, grid, block, 0, s, a); break;

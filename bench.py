@@ -45,6 +45,12 @@ def parse():
     p.add_argument("--no-phase-timing", action="store_true")
     p.add_argument("--matrices", type=int, default=0,
                    help="use only the first N matrices of the workload (diagnostics; 0 = all)")
+    p.add_argument("--adamw", action="store_true",
+                   help="also time one AdamW step (float32 moments) over the same parameters, "
+                        "for the Muon/AdamW optimizer-step ratio")
+    p.add_argument("--place-ranks", type=int, default=0,
+                   help="also place the matrices on R simulated data-parallel ranks, round robin "
+                        "vs LPT, with costs measured per matrix shape (0 = off)")
     return p.parse_args()
 
 
@@ -93,6 +99,62 @@ def cpu_baseline(wl, budget_s):
                   f"({', '.join(sorted(set(s for s, _ in done)))}) of the same workload, "
                   f"{busy:.1f} s of CPU time",
     }
+
+
+def measure_placement(mu, M, wl, ranks, mode):
+    """Per-matrix Newton-Schulz cost measured on the GPU for every distinct
+    shape (muon_ns_batched over up to 64 matrices of that shape, median of 3
+    runs), then the placement of all matrices on `ranks` ranks, round robin
+    against LPT (muon_place)."""
+    import statistics
+    import torch
+    by_shape = {}
+    for i, t in enumerate(M):
+        by_shape.setdefault(tuple(t.shape), []).append(i)
+    per_ms = {}
+    for shape, idx in by_shape.items():
+        sub = [M[i].clone() for i in idx[:64]]
+        cb = [wl.col_blocks] * len(sub)
+        mu.muon_ns_batched(sub, iters=wl.iters, mode=mode, col_blocks=cb)  # warm-up
+        runs = []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            mu.muon_ns_batched(sub, iters=wl.iters, mode=mode, col_blocks=cb)
+            torch.cuda.synchronize()
+            runs.append((time.perf_counter() - t0) * 1e3 / len(sub))
+        per_ms[shape] = statistics.median(runs)
+        del sub
+    costs = [per_ms[tuple(t.shape)] for t in M]
+    out = {"ranks": ranks,
+           "cost": "measured muon_ns_batched ms per matrix, by shape (up to 64 matrices, median of 3)",
+           "ms_per_matrix": {f"{r}x{c}": round(v, 4) for (r, c), v in per_ms.items()}}
+    for pol in ("rr", "lpt"):
+        _, load, imb = mu.muon_place(costs, ranks, pol)
+        out[pol] = {"max_rank_ms": round(max(load), 3), "imbalance": round(imb, 4)}
+    return out
+
+
+def measure_adamw(mu, W, G, steps, warmup):
+    """Time muon_adamw_step over the workload's parameters with float32
+    moments; HBM bytes per element: read W, g, m, v and write W, m, v."""
+    import torch
+    Mo = [torch.zeros(t.shape, dtype=torch.float32, device=t.device) for t in W]
+    V = [torch.zeros(t.shape, dtype=torch.float32, device=t.device) for t in W]
+    kw = dict(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    for k in range(warmup):
+        mu.muon_adamw_step(W, G, Mo, V, step=k + 1, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        mu.muon_adamw_step(W, G, Mo, V, step=warmup + k + 1, **kw)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    es = W[0].element_size()
+    nbytes = sum(t.numel() for t in W) * (3 * es + 16)
+    return {"ms_per_step": round(ms, 3), "moments": "float32",
+            "bytes_per_step": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def recorded_traffic(workload, kernel):
@@ -205,7 +267,8 @@ def main():
         "pct_peak_nominal": round(100 * tflops_nom / PEAK_BF16_TFLOPS, 2),
     }
     if phases:
-        per_step = {k: (v[0] / args.steps, v[1] // max(args.steps, 1)) for k, v in phases.items()}
+        per_step = {k: (v[0] / args.steps, v[1] // max(args.steps, 1)) for k, v in phases.items()
+                    if k != "adamw"}
         out["phase_ms_per_step"] = {k: round(v[0], 3) for k, v in per_step.items()}
         out["launches_per_step"] = {k: int(v[1]) for k, v in per_step.items()}
         ns_ms = sum(per_step[k][0] for k in ("norm", "gram", "aa", "bx"))
@@ -236,6 +299,16 @@ def main():
         el_bytes = acc.elementwise_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4)
         el_ms = per_step["prep"][0] + per_step["finish"][0]
         out["elementwise_gbs"] = round(el_bytes / (el_ms * 1e-3) / 1e9, 1) if el_ms > 0 else None
+    if args.place_ranks > 0:
+        print(f"[bench] placement over {args.place_ranks} simulated ranks", file=sys.stderr, flush=True)
+        out["placement"] = measure_placement(mu, M, wl, args.place_ranks, mode)
+    if args.adamw:
+        print("[bench] timing AdamW over the same parameters", file=sys.stderr, flush=True)
+        del ws
+        M.clear()
+        torch.cuda.empty_cache()
+        out["adamw"] = measure_adamw(mu, W, G, args.steps, args.warmup)
+        out["adamw"]["muon_over_adamw"] = round(ms_step / out["adamw"]["ms_per_step"], 2)
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

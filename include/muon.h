@@ -178,12 +178,12 @@ const char *muon_last_error(void);
  * kernel launch the library makes on this thread is bracketed by a pair of
  * HIP events recorded on the call's stream. muon_phase_times() waits for the
  * recorded events, writes each kernel kind's summed milliseconds and launch
- * count into ms[6] and launches[6] (order: prep, norm, gram, aa, bx, finish;
- * either pointer may be NULL) and clears the record. Events are created by
+ * count into ms[7] and launches[7] (order: prep, norm, gram, aa, bx, finish,
+ * adamw; either pointer may be NULL) and clears the record. Events are created by
  * the library on first use and reused; no device memory is allocated.
  */
 muon_status muon_set_phase_timing(int32_t enable);
-muon_status muon_phase_times(double ms[6], int64_t launches[6]);
+muon_status muon_phase_times(double ms[7], int64_t launches[7]);
 
 /*
  * Host-only description of how a call would be scheduled, as JSON written
@@ -195,6 +195,59 @@ muon_status muon_phase_times(double ms[6], int64_t launches[6]);
  */
 muon_status muon_plan_info(const muon_mat *descs, int32_t n_mats, int32_t iters, uint32_t mode,
                            size_t workspace_bytes, char *buf, size_t len, size_t *needed);
+
+/*
+ * One AdamW step for n_mats matrices: the optimizer the pages measure Muon
+ * against (Table 1 of the blog post: AdamW and Muon training throughput on
+ * the same models), for a like-for-like optimizer-step time on one GPU. The
+ * pages do not restate it; this is the published algorithm (Adam's
+ * bias-corrected moments, Kingma and Ba, Algorithm 1; decoupled weight
+ * decay, Loshchilov and Hutter, Algorithm 2), element by element:
+ *   m <- beta1 m + (1 - beta1) g
+ *   v <- beta2 v + (1 - beta2) g^2
+ *   W <- W (1 - lr weight_decay) - lr / (1 - beta1^step) * m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ * in float32 arithmetic.
+ *   params      W, updated in place; all F32 or all BF16.
+ *   grads       g, read only; the dtype of params.
+ *   exp_avg     m, float32, updated in place.
+ *   exp_avg_sq  v, float32, updated in place.
+ *               The four descriptors of matrix i share rows and cols
+ *               (pitches may differ); written buffers may not overlap any
+ *               other buffer of the call.
+ *   lr, weight_decay  finite;  beta1, beta2 in [0, 1);  eps finite, > 0;
+ *   step        1-based count of this step (bias correction), >= 1.
+ * Needs no workspace. n_mats == 0 is a no-op. Launches are timed under the
+ * "adamw" kind of muon_phase_times.
+ */
+muon_status muon_adamw_step(const muon_mat *params, const muon_mat *grads, const muon_mat *exp_avg,
+                            const muon_mat *exp_avg_sq, int32_t n_mats, float lr, float beta1,
+                            float beta2, float eps, float weight_decay, int32_t step);
+
+/*
+ * Placement of whole matrices on `ranks` data-parallel ranks, each of which
+ * would then run muon_step on its share (layer-wise distribution: [zh]
+ * section "逐层分布式优化器"). Perfect balance is not reachable in general;
+ * the pages place matrices round robin today and expect estimated costs to
+ * do better ([zh] section "负载均衡"):
+ *   MUON_PLACE_RR   matrix i goes to rank i mod ranks;
+ *   MUON_PLACE_LPT  matrices in descending cost (ties: lower index first)
+ *                   each go to the rank with the least cost so far (ties:
+ *                   lower rank), the longest-processing-time-first rule.
+ *   costs      host array of n_mats finite costs >= 0 (measured times, or the
+ *              cost model of muon_plan_info), read only.
+ *   ranks      1 .. 65536.
+ *   owner      host array of n_mats, receives each matrix's rank.
+ *   load       host array of `ranks` (or NULL), receives each rank's summed
+ *              cost.
+ *   imbalance  (or NULL) receives max(load) / mean(load); 1 when every cost
+ *              is 0.
+ * Host only; launches nothing. Invalid arguments: MUON_ERR_INVALID_ARG,
+ * nothing written.
+ */
+#define MUON_PLACE_RR 0u
+#define MUON_PLACE_LPT 1u
+muon_status muon_place(const double *costs, int32_t n_mats, int32_t ranks, uint32_t policy,
+                       int32_t *owner, double *load, double *imbalance);
 
 #ifdef __cplusplus
 }

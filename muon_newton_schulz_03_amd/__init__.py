@@ -32,6 +32,8 @@ MUON_NS_FULL = 0x000
 MUON_NS_BLOCKWISE = 0x001
 MUON_PACK_RR = 0x000
 MUON_PACK_COST = 0x010
+MUON_PLACE_RR = 0
+MUON_PLACE_LPT = 1
 MUON_AA_PLAIN = 0x000
 MUON_AA_SPLIT = 0x100
 
@@ -42,8 +44,9 @@ EXPORTED = (
     "muon_ns_batched", "muon_step", "muon_set_stream", "muon_workspace_size",
     "muon_workspace_min_size", "muon_set_workspace", "muon_set_step_options",
     "muon_last_error", "muon_plan_info", "muon_set_phase_timing", "muon_phase_times",
+    "muon_place", "muon_adamw_step",
 )
-PHASES = ("prep", "norm", "gram", "aa", "bx", "finish")
+PHASES = ("prep", "norm", "gram", "aa", "bx", "finish", "adamw")
 
 
 class MuonError(RuntimeError):
@@ -91,6 +94,11 @@ def load_library(path=LIB_PATH):
                             ctypes.c_char_p, ctypes.c_size_t, sz], ctypes.c_int),
         "muon_set_phase_timing": ([ctypes.c_int32], ctypes.c_int),
         "muon_phase_times": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+        "muon_adamw_step": ([mat_p, mat_p, mat_p, mat_p, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                             ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int32], ctypes.c_int),
+        "muon_place": ([ctypes.POINTER(ctypes.c_double), ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
+                        ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -201,10 +209,23 @@ def muon_set_phase_timing(enable=True):
 
 def muon_phase_times():
     """{kind: (milliseconds, launches)} since the last query (see muon.h)."""
-    ms = (ctypes.c_double * 6)()
-    n = (ctypes.c_int64 * 6)()
+    ms = (ctypes.c_double * len(PHASES))()
+    n = (ctypes.c_int64 * len(PHASES))()
     _check(lib().muon_phase_times(ms, n))
     return {k: (ms[i], n[i]) for i, k in enumerate(PHASES)}
+
+
+def muon_place(costs, ranks, policy="lpt"):
+    """Place matrices with the given costs on `ranks` ranks (see muon.h).
+    Returns (owner list, per-rank load list, max/mean imbalance)."""
+    n = len(costs)
+    c = (ctypes.c_double * max(n, 1))(*[float(x) for x in costs])
+    owner = (ctypes.c_int32 * max(n, 1))()
+    load = (ctypes.c_double * ranks)()
+    imb = ctypes.c_double()
+    pol = {"rr": MUON_PLACE_RR, "lpt": MUON_PLACE_LPT}[policy] if isinstance(policy, str) else policy
+    _check(lib().muon_place(c, n, ranks, pol, owner, load, ctypes.byref(imb)))
+    return list(owner[:n]), list(load), imb.value
 
 
 # ---------------------------------------------------------------------------
@@ -275,3 +296,16 @@ def muon_step(params, grads, moms, lr=0.02, beta=0.95, nesterov=False, iters=5, 
     else:
         muon_set_workspace(workspace.data_ptr(), workspace.numel() * workspace.element_size())
     _check(lib().muon_step(mats(W), mats(G), mats(M), len(W), lr, beta, 1 if nesterov else 0))
+
+
+def muon_adamw_step(params, grads, exp_avg, exp_avg_sq, lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                    weight_decay=0.0, step=1):
+    """One AdamW step over lists of 2-D device tensors (see muon.h): params
+    (bf16 or float32) and the float32 moments are updated in place."""
+    W = [mat_of(t) for t in params]
+    G = [mat_of(t) for t in grads]
+    Mo = [mat_of(t) for t in exp_avg]
+    V = [mat_of(t) for t in exp_avg_sq]
+    muon_set_stream(None)
+    _check(lib().muon_adamw_step(mats(W), mats(G), mats(Mo), mats(V), len(W), lr, beta1, beta2, eps,
+                                 weight_decay, step))

@@ -36,7 +36,7 @@ struct Timing {
 };
 thread_local Timing g_timing;
 
-enum TimedKind { kTPrep = 0, kTNorm, kTGram, kTAA, kTBX, kTFinish, kTKinds };
+enum TimedKind { kTPrep = 0, kTNorm, kTGram, kTAA, kTBX, kTFinish, kTAdamW, kTKinds };
 
 // Runs `launch` (returning hipError_t) bracketed by events when timing is on.
 template <class F>
@@ -365,7 +365,7 @@ muon_status muon_set_phase_timing(int32_t enable) {
   return ok();
 }
 
-muon_status muon_phase_times(double ms[6], int64_t launches[6]) {
+muon_status muon_phase_times(double ms[7], int64_t launches[7]) {
   double acc[kTKinds] = {};
   int64_t cnt[kTKinds] = {};
   for (size_t i = 0; i < g_timing.kinds.size(); ++i) {
@@ -402,6 +402,122 @@ muon_status muon_plan_info(const muon_mat *descs, int32_t n_mats, int32_t iters,
     std::memcpy(buf, js.data(), n);
     buf[n] = 0;
   }
+  return ok();
+}
+
+muon_status muon_place(const double *costs, int32_t n_mats, int32_t ranks, uint32_t policy,
+                       int32_t *owner, double *load, double *imbalance) {
+  if (n_mats < 0 || n_mats > kMaxMats) return fail(MUON_ERR_INVALID_ARG, "n_mats out of range");
+  if (ranks < 1 || ranks > 65536) return fail(MUON_ERR_INVALID_ARG, "ranks out of range [1, 65536]");
+  if (policy != MUON_PLACE_RR && policy != MUON_PLACE_LPT) return fail(MUON_ERR_INVALID_ARG, "unknown policy");
+  if (n_mats > 0 && (!costs || !owner)) return fail(MUON_ERR_INVALID_ARG, "costs and owner must not be NULL");
+  for (int32_t i = 0; i < n_mats; ++i)
+    if (!std::isfinite(costs[i]) || costs[i] < 0)
+      return fail(MUON_ERR_INVALID_ARG, "costs must be finite and >= 0 (index " + std::to_string(i) + ")");
+  std::vector<double> ld(static_cast<size_t>(ranks));
+  std::vector<int32_t> own(static_cast<size_t>(n_mats));
+  place(costs, n_mats, ranks, policy, own.data(), ld.data());
+  for (int32_t i = 0; i < n_mats; ++i) owner[i] = own[size_t(i)];
+  if (load)
+    for (int32_t r = 0; r < ranks; ++r) load[r] = ld[size_t(r)];
+  if (imbalance) {
+    double mx = 0, sum = 0;
+    for (double v : ld) {
+      mx = v > mx ? v : mx;
+      sum += v;
+    }
+    *imbalance = sum > 0 ? mx / (sum / ranks) : 1.0;
+  }
+  return ok();
+}
+
+muon_status muon_adamw_step(const muon_mat *params, const muon_mat *grads, const muon_mat *exp_avg,
+                            const muon_mat *exp_avg_sq, int32_t n_mats, float lr, float beta1, float beta2,
+                            float eps, float weight_decay, int32_t step) {
+  Error err;
+  if (n_mats < 0 || n_mats > kMaxMats) return fail(MUON_ERR_INVALID_ARG, "n_mats out of range");
+  if (n_mats > 0 && (!params || !grads || !exp_avg || !exp_avg_sq))
+    return fail(MUON_ERR_INVALID_ARG, "descriptor arrays must not be NULL");
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay))
+    return fail(MUON_ERR_INVALID_ARG, "lr and weight_decay must be finite");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+    return fail(MUON_ERR_INVALID_ARG, "beta1 and beta2 must lie in [0, 1)");
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (step < 1) return fail(MUON_ERR_INVALID_ARG, "step must be >= 1");
+  if (n_mats == 0) return ok();
+  const int32_t pdt = params[0].dtype;
+  if (pdt != MUON_F32 && pdt != MUON_BF16) return fail(MUON_ERR_DTYPE, "params: unknown dtype");
+  const size_t pes = dtype_size(pdt);
+  for (int32_t i = 0; i < n_mats; ++i) {
+    const muon_mat *ds[4] = {&params[i], &grads[i], &exp_avg[i], &exp_avg_sq[i]};
+    const char *names[4] = {"params", "grads", "exp_avg", "exp_avg_sq"};
+    for (int k = 0; k < 4; ++k) {
+      const muon_mat &d = *ds[k];
+      const std::string at = std::string(names[k]) + "[" + std::to_string(i) + "]";
+      const int32_t want = k < 2 ? pdt : int32_t(MUON_F32);
+      if (d.dtype != want)
+        return fail(MUON_ERR_DTYPE, at + ": params and grads share one dtype; exp_avg and exp_avg_sq are float32");
+      if (!d.data) return fail(MUON_ERR_INVALID_ARG, at + ": NULL data");
+      if (d.rows <= 0 || d.cols <= 0 || d.ld < d.cols)
+        return fail(MUON_ERR_SHAPE, at + ": rows, cols must be > 0 and ld >= cols");
+      if (d.rows != params[i].rows || d.cols != params[i].cols)
+        return fail(MUON_ERR_SHAPE, at + ": shape differs from params[" + std::to_string(i) + "]");
+      if (reinterpret_cast<uintptr_t>(d.data) % dtype_size(d.dtype))
+        return fail(MUON_ERR_ALIGN, at + ": data not aligned to its element size");
+    }
+    if (params[i].rows * ((params[i].cols + 7) / 8) > (int64_t(1) << 30))
+      return fail(MUON_ERR_SHAPE, "params[" + std::to_string(i) + "]: more than 2^33 elements");
+  }
+  const muon_mat *arrays[4] = {params, exp_avg, exp_avg_sq, grads};
+  const bool writable[4] = {true, true, true, false};
+  if (!check_alias(arrays, writable, 4, n_mats, &err)) return fail(err);
+
+  const double bc1 = 1.0 - std::pow(double(beta1), double(step));
+  const double bc2 = 1.0 - std::pow(double(beta2), double(step));
+  AdamArgs a{};
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.eps = eps;
+  a.decay = float(1.0 - double(lr) * double(weight_decay));
+  a.step_size = float(double(lr) / bc1);
+  a.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
+  hipStream_t st = g_state.stream;
+  auto flush = [&]() -> muon_status {
+    hipError_t e = timed(kTAdamW, st, [&] { return launch_adamw(a, pdt == MUON_BF16, st); });
+    a.nv = 0;
+    a.total_chunks = 0;
+    return e == hipSuccess ? MUON_OK : hip_fail(e, "adamw launch");
+  };
+  auto rows16 = [](const void *p, int64_t ld, size_t es) {
+    return reinterpret_cast<uintptr_t>(p) % 16 == 0 && (size_t(ld) * es) % 16 == 0;
+  };
+  for (int32_t i = 0; i < n_mats; ++i) {
+    const int64_t cpr = (params[i].cols + 7) / 8;
+    const int64_t chunks = params[i].rows * cpr;
+    if (a.nv == kElemViewsMax || int64_t(a.total_chunks) + chunks > (int64_t(1) << 31) - 256) {
+      muon_status s = flush();
+      if (s != MUON_OK) return s;
+    }
+    AdamView &v = a.v[a.nv];
+    v = AdamView{};
+    v.w = params[i].data;
+    v.g = grads[i].data;
+    v.m = static_cast<float *>(exp_avg[i].data);
+    v.v = static_cast<float *>(exp_avg_sq[i].data);
+    v.ld_w = params[i].ld;
+    v.ld_g = grads[i].ld;
+    v.ld_m = exp_avg[i].ld;
+    v.ld_v = exp_avg_sq[i].ld;
+    v.rows = int32_t(params[i].rows);
+    v.cols = int32_t(params[i].cols);
+    v.chunks_per_row = int32_t(cpr);
+    v.chunk_begin = a.total_chunks;
+    v.vec = (params[i].cols % 8 == 0 && rows16(v.w, v.ld_w, pes) && rows16(v.g, v.ld_g, pes) &&
+             rows16(v.m, v.ld_m, 4) && rows16(v.v, v.ld_v, 4)) ? 1 : 0;
+    a.total_chunks += int32_t(chunks);
+    a.nv++;
+  }
+  if (a.nv) return flush();
   return ok();
 }
 

@@ -84,9 +84,34 @@ struct GemmArgs {
   float eps;
 };
 
-// Launchers (kernels.hip). Each returns the HIP error of the launch.
+// AdamW (the comparator): one element-wise launch over up to kElemViewsMax
+// matrices; each thread updates one run of 8 consecutive elements of a row.
+struct AdamView {
+  void *w;                     // parameters (T)
+  const void *g;               // gradients (T)
+  float *m, *v;                // first and second moments (float32)
+  int64_t ld_w, ld_g, ld_m, ld_v;
+  int32_t rows, cols;
+  int32_t chunks_per_row;      // ceil(cols / 8)
+  int32_t chunk_begin;         // first chunk of this matrix in the launch
+  int32_t vec;                 // every row of every buffer holds whole aligned runs of 8
+  int32_t pad_;
+};
+
+struct AdamArgs {
+  AdamView v[kElemViewsMax];
+  int32_t nv;
+  int32_t total_chunks;
+  float beta1, beta2, eps;
+  float decay;                 // 1 - lr * weight_decay
+  float step_size;             // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;          // 1 / sqrt(1 - beta2^t)
+};
+
+// Launchers (kernels.hip, adamw.hip). Each returns the HIP error of the launch.
 hipError_t launch_elem(const ElemArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_norm_finalize(const GemmArgs &a, int views, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &a, int phase, bool bf16, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs &a, bool bf16, hipStream_t s);
 
 }  // namespace muon

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <numeric>
+#include <queue>
 #include <sstream>
 
 namespace muon {
@@ -272,6 +273,33 @@ std::string plan_json(const Plan &p) {
   }
   o << "]}";
   return o.str();
+}
+
+void place(const double *costs, int32_t n, int32_t ranks, uint32_t policy, int32_t *owner,
+           double *load) {
+  for (int32_t r = 0; r < ranks; ++r) load[r] = 0.0;
+  if (policy == MUON_PLACE_RR) {
+    for (int32_t i = 0; i < n; ++i) {
+      owner[i] = i % ranks;
+      load[i % ranks] += costs[i];
+    }
+    return;
+  }
+  std::vector<int32_t> order(static_cast<size_t>(n));
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return costs[a] > costs[b]; });
+  // min-heap of (load, rank): the least-loaded rank, lower rank on ties
+  using Item = std::pair<double, int32_t>;
+  std::priority_queue<Item, std::vector<Item>, std::greater<Item>> heap;
+  for (int32_t r = 0; r < ranks; ++r) heap.push({0.0, r});
+  for (int32_t i : order) {
+    Item it = heap.top();
+    heap.pop();
+    owner[i] = it.second;
+    it.first += costs[i];
+    load[it.second] = it.first;
+    heap.push(it);
+  }
 }
 
 }  // namespace muon

@@ -107,6 +107,11 @@ bool build_plan(const muon_mat *d, int32_t n, int32_t iters, uint32_t mode, size
 
 std::string plan_json(const Plan &p);
 
+// Placement of n costs on `ranks` ranks (policy 0: round robin, 1: LPT);
+// writes owner[n] and load[ranks]. Arguments are validated by the caller.
+void place(const double *costs, int32_t n, int32_t ranks, uint32_t policy, int32_t *owner,
+           double *load);
+
 // Exact element-overlap test of two strided matrices (byte addresses).
 bool matrices_overlap(const muon_mat &a, const muon_mat &b);
 

@@ -1,4 +1,5 @@
-"""CPU oracle for the Muon optimizer step (test infrastructure only).
+"""CPU oracle for the Muon optimizer step, and for the AdamW step it is
+compared against (test infrastructure only).
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package. The library itself never calls it, and it shares no code
@@ -16,3 +17,4 @@ from .muon_oracle import (  # noqa: F401
     muon_step,
     newton_schulz_iteration_rows,
 )
+from .adamw_oracle import adamw_step  # noqa: F401,E402

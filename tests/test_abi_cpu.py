@@ -79,6 +79,30 @@ def test_ns_validation_codes(lib):
         assert lib.muon_set_step_options(5, cf, 1e-7, 0) == mu.MUON_ERR_INVALID_ARG
 
 
+def test_adamw_validation_codes(lib):
+    """Every invalid AdamW call is rejected on the host, before any launch."""
+    def call(W, G, Mo, V, lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.0, step=1, n=None):
+        k = len(W) if n is None else n
+        return lib.muon_adamw_step(mu.mats(W), mu.mats(G), mu.mats(Mo), mu.mats(V), k, lr, b1, b2, eps, wd, step)
+    bf, f32 = mu.MUON_BF16, mu.MUON_F32
+    W = [desc(4, 8, dtype=bf, ptr=FAKE)]
+    G = [desc(4, 8, dtype=bf, ptr=FAKE * 2)]
+    Mo = [desc(4, 8, dtype=f32, ptr=FAKE * 3)]
+    V = [desc(4, 8, dtype=f32, ptr=FAKE * 4)]
+    assert call([], [], [], [], n=0) == mu.MUON_OK
+    assert call(W, G, Mo, V, n=-1) == mu.MUON_ERR_INVALID_ARG
+    assert call(W, G, Mo, V, b1=1.0) == mu.MUON_ERR_INVALID_ARG
+    assert call(W, G, Mo, V, b2=-0.1) == mu.MUON_ERR_INVALID_ARG
+    assert call(W, G, Mo, V, eps=0.0) == mu.MUON_ERR_INVALID_ARG
+    assert call(W, G, Mo, V, lr=float("nan")) == mu.MUON_ERR_INVALID_ARG
+    assert call(W, G, Mo, V, step=0) == mu.MUON_ERR_INVALID_ARG
+    assert call(W, G, [desc(4, 8, dtype=bf, ptr=FAKE * 3)], V) == mu.MUON_ERR_DTYPE
+    assert call(W, [desc(4, 8, dtype=f32, ptr=FAKE * 2)], Mo, V) == mu.MUON_ERR_DTYPE
+    assert call(W, G, Mo, [desc(4, 9, dtype=f32, ptr=FAKE * 4)]) == mu.MUON_ERR_SHAPE
+    assert call(W, G, Mo, [desc(4, 8, dtype=f32, ptr=FAKE * 4 + 2)]) == mu.MUON_ERR_ALIGN
+    assert call(W, G, [desc(4, 8, dtype=f32, ptr=FAKE + 16)], V) == mu.MUON_ERR_ALIAS
+
+
 def test_alias_exact_for_interleaved_views(lib):
     # two column blocks of one 8 x 64 bf16 buffer do not overlap element-wise
     left = desc(8, 32, ld=64)

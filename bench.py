@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-phase-timing", action="store_true")
     p.add_argument("--matrices", type=int, default=0,
                    help="use only the first N matrices of the workload (diagnostics; 0 = all)")
+    p.add_argument("--tp", type=int, default=0,
+                   help="simulate the tensor-parallel (distributed) mode with this many column "
+                        "shards per matrix on this one GPU; tall matrices enter transposed")
     p.add_argument("--adamw", action="store_true",
                    help="also time one AdamW step (float32 moments) over the same parameters, "
                         "for the Muon/AdamW optimizer-step ratio")
@@ -54,7 +57,7 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(wl, budget_s):
+def cpu_baseline(wl, budget_s, col_blocks=None):
     """Time the CPU oracle (float32) on matrices of the workload until the
     budget is spent; report algorithmic TFLOP/s."""
     import numpy as np
@@ -68,6 +71,7 @@ def cpu_baseline(wl, budget_s):
         threads = 0
     if not threads:
         threads = len(os.sched_getaffinity(0))
+    cb = wl.col_blocks if col_blocks is None else col_blocks
     rng = np.random.default_rng(wl.seed)
     shapes = list(dict.fromkeys(wl.shapes))  # distinct shapes, in order
     flops = 0.0
@@ -81,9 +85,9 @@ def cpu_baseline(wl, budget_s):
         W = (rng.standard_normal((r, c)) * wl.std_w).astype(np.float32)
         t = time.perf_counter()
         oracle.muon_step(W, G, M, lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov, iters=wl.iters,
-                         col_blocks=wl.col_blocks, dtype=np.float32)
+                         col_blocks=cb, dtype=np.float32)
         el = time.perf_counter() - t
-        f = sum(acc.flops_algorithmic(*acc.wide(*v), wl.iters) for v in acc.views([(r, c)], wl.col_blocks))
+        f = sum(acc.flops_algorithmic(*acc.wide(*v), wl.iters) for v in acc.views([(r, c)], cb))
         flops += f
         done.append((f"{r}x{c}", el))
         i += 1
@@ -194,7 +198,14 @@ def main():
     torch.cuda.set_device(dev)
     mode = (mu.MUON_PACK_COST if args.pack == "cost" else mu.MUON_PACK_RR)
     mode |= mu.MUON_AA_SPLIT if args.aa == "split" else mu.MUON_AA_PLAIN
-    if wl.col_blocks > 1:
+    if args.tp > 0:
+        import dataclasses
+        # distributed mode shards the long side of wide matrices: a tall
+        # matrix enters transposed (same Newton-Schulz work)
+        wl = dataclasses.replace(wl, name=f"{wl.name}_tp{args.tp}", col_blocks=args.tp,
+                                 shapes=[(min(r, c), max(r, c)) for r, c in wl.shapes])
+        mode |= mu.MUON_NS_DISTRIBUTED
+    elif wl.col_blocks > 1:
         mode |= mu.MUON_NS_BLOCKWISE
     print(f"[bench] workload {wl.name}: {len(wl.shapes)} matrices; generating inputs", file=sys.stderr,
           flush=True)
@@ -233,8 +244,9 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
     print(f"[bench] {args.steps} steps, {ms_step:.2f} ms/step", file=sys.stderr, flush=True)
 
-    f_nom, f_alg = acc.workload_flops(wl.shapes, wl.iters, wl.col_blocks)
-    g_f, a_f, b_f = acc.workload_phase_flops(wl.shapes, wl.col_blocks)
+    blocks = 1 if args.tp > 0 else wl.col_blocks  # distributed mode computes the whole matrix
+    f_nom, f_alg = acc.workload_flops(wl.shapes, wl.iters, blocks)
+    g_f, a_f, b_f = acc.workload_phase_flops(wl.shapes, blocks)
     tflops_alg = f_alg / (ms_step * 1e-3) / 1e12
     tflops_nom = f_nom / (ms_step * 1e-3) / 1e12
 
@@ -258,6 +270,7 @@ def main():
             "col_blocks": wl.col_blocks,
             "iters": wl.iters,
             "pack": args.pack,
+            "tp": args.tp,
             "aa": args.aa,
             "workspace_gib": round(ws_bytes / 2**30, 2),
             "groups": len(plan["chunks"]),
@@ -268,7 +281,7 @@ def main():
     }
     if phases:
         per_step = {k: (v[0] / args.steps, v[1] // max(args.steps, 1)) for k, v in phases.items()
-                    if k != "adamw"}
+                    if k not in ("adamw", "reduce") or v[1] > 0}
         out["phase_ms_per_step"] = {k: round(v[0], 3) for k, v in per_step.items()}
         out["launches_per_step"] = {k: int(v[1]) for k, v in per_step.items()}
         ns_ms = sum(per_step[k][0] for k in ("norm", "gram", "aa", "bx"))
@@ -299,6 +312,18 @@ def main():
         el_bytes = acc.elementwise_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4)
         el_ms = per_step["prep"][0] + per_step["finish"][0]
         out["elementwise_gbs"] = round(el_bytes / (el_ms * 1e-3) / 1e9, 1) if el_ms > 0 else None
+    if args.tp > 0 and phases:
+        P = args.tp
+        red = per_step.get("reduce", (0.0, 0))[0]
+        out["distributed"] = {
+            "shards": P,
+            "note": "all P shards run on this GPU; A*A runs once per shard (redundantly, as on every rank); "
+                    "the packed-triangle sum stands in for the all-reduce",
+            "reduce_ms_per_step": round(red, 3),
+            "per_rank_ms_estimate": round((per_step["gram"][0] + per_step["aa"][0] + per_step["bx"][0]
+                                           + per_step["prep"][0] + per_step["finish"][0]) / P
+                                          + per_step["norm"][0] + red / P, 3),
+        }
     if args.place_ranks > 0:
         print(f"[bench] placement over {args.place_ranks} simulated ranks", file=sys.stderr, flush=True)
         out["placement"] = measure_placement(mu, M, wl, args.place_ranks, mode)
@@ -311,7 +336,7 @@ def main():
         out["adamw"]["muon_over_adamw"] = round(ms_step / out["adamw"]["ms_per_step"], 2)
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, col_blocks=blocks)
     print(json.dumps(out), flush=True)
 
 

@@ -74,6 +74,9 @@ typedef struct muon_mat {
 #define MUON_NS_FULL 0x000u      /* orthogonalize each whole matrix          */
 #define MUON_NS_BLOCKWISE 0x001u /* orthogonalize col_blocks column blocks of
                                     each matrix independently                */
+#define MUON_NS_DISTRIBUTED 0x002u /* the whole-matrix result, computed as
+                                    col_blocks column shards that share one
+                                    Gram per iteration (see below)           */
 #define MUON_PACK_RR 0x000u      /* matrices enter the grouped launches in the
                                     order given (round robin)                */
 #define MUON_PACK_COST 0x010u    /* ... in descending cost order             */
@@ -108,6 +111,19 @@ typedef struct muon_mat {
  *           All finite, c != 0 and b / c finite (B is formed as
  *           c (A A + (b / c) A)); otherwise MUON_ERR_INVALID_ARG.
  *   mode    MUON_NS_* | MUON_PACK_* | MUON_AA_* bits.
+ *
+ * MUON_NS_DISTRIBUTED simulates, on one GPU, the pages' tensor-parallel
+ * ("distributed") mode ([zh] section "Distributed mode"; [pt] section
+ * "2. Newton-Schulz distribuído"): each matrix (rows <= cols; pass a tall
+ * matrix transposed) is split into P = col_blocks column shards X_p, every
+ * matrix of the call with the same P. Per iteration each shard forms its
+ * partial Gram X_p X_p^T; the partials are exchanged as packed upper
+ * triangles ([zh] section "SYRK 和融合的 all-reduce": float32, row i holding
+ * columns i .. mp - 1, mp the padded row count) and summed in shard order,
+ * standing in for the all-reduce; every shard then forms B from the full A
+ * (redundantly, as every rank would) and updates its own columns. The norm
+ * is the whole matrix's. The result is the full-matrix Newton-Schulz up to
+ * rounding order. Shard partial Grams keep their bf16 lo half.
  *   eps     taken from muon_set_step_options (default 1e-7).
  * n_mats == 0 is a no-op returning MUON_OK.
  */
@@ -178,12 +194,12 @@ const char *muon_last_error(void);
  * kernel launch the library makes on this thread is bracketed by a pair of
  * HIP events recorded on the call's stream. muon_phase_times() waits for the
  * recorded events, writes each kernel kind's summed milliseconds and launch
- * count into ms[7] and launches[7] (order: prep, norm, gram, aa, bx, finish,
- * adamw; either pointer may be NULL) and clears the record. Events are created by
+ * count into ms[8] and launches[8] (order: prep, norm, gram, aa, bx, finish,
+ * adamw, reduce; either pointer may be NULL) and clears the record. Events are created by
  * the library on first use and reused; no device memory is allocated.
  */
 muon_status muon_set_phase_timing(int32_t enable);
-muon_status muon_phase_times(double ms[7], int64_t launches[7]);
+muon_status muon_phase_times(double ms[8], int64_t launches[8]);
 
 /*
  * Host-only description of how a call would be scheduled, as JSON written

@@ -30,6 +30,7 @@ MUON_BF16 = 1
 
 MUON_NS_FULL = 0x000
 MUON_NS_BLOCKWISE = 0x001
+MUON_NS_DISTRIBUTED = 0x002
 MUON_PACK_RR = 0x000
 MUON_PACK_COST = 0x010
 MUON_PLACE_RR = 0
@@ -46,7 +47,7 @@ EXPORTED = (
     "muon_last_error", "muon_plan_info", "muon_set_phase_timing", "muon_phase_times",
     "muon_place", "muon_adamw_step",
 )
-PHASES = ("prep", "norm", "gram", "aa", "bx", "finish", "adamw")
+PHASES = ("prep", "norm", "gram", "aa", "bx", "finish", "adamw", "reduce")
 
 
 class MuonError(RuntimeError):

@@ -36,7 +36,7 @@ struct Timing {
 };
 thread_local Timing g_timing;
 
-enum TimedKind { kTPrep = 0, kTNorm, kTGram, kTAA, kTBX, kTFinish, kTAdamW, kTKinds };
+enum TimedKind { kTPrep = 0, kTNorm, kTGram, kTAA, kTBX, kTFinish, kTAdamW, kTReduce, kTKinds };
 
 // Runs `launch` (returning hipError_t) bracketed by events when timing is on.
 template <class F>
@@ -124,11 +124,14 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
     ga.r = coeffs[1] / coeffs[2];
     ga.eps = eps;
     ga.aa_plain = (plan.mode & MUON_AA_SPLIT) ? 0 : 1;
+    ga.group = plan.distributed ? plan.shards : 1;
+    // a shard's partial Gram keeps its lo half: it goes into a sum
+    ga.gram_halves = (ga.aa_plain && !plan.distributed) ? 1 : 2;
     ga.remap = 1;
     int32_t view_begin = 0;
     for (size_t s = 0; s < ch.segs.size(); ++s) {
       const Segment &sg = ch.segs[s];
-      const Layout L = view_layout(sg.mp, sg.np, bf16);
+      const Layout L = view_layout(sg.mp, sg.np, bf16, plan.distributed);
       GemmSeg &g = ga.seg[s];
       g.base = ws + sg.base;
       g.stride = int64_t(sg.stride);
@@ -139,6 +142,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       g.off_bdiag = int64_t(L.bdiag);
       g.off_part = int64_t(L.partials);
       g.off_scale = int64_t(L.scale);
+      g.off_tri = int64_t(L.tri);
       g.mp = int32_t(sg.mp);
       g.np = int32_t(sg.np);
       g.count = sg.count;
@@ -238,6 +242,28 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       set_tiles(true);
       e = timed(kTGram, st, [&] { return launch_gemm(ga, kGram, bf16, st); });
       if (e != hipSuccess) return hip_fail(e, "gram launch");
+      if (plan.distributed) {
+        // the all-reduce of the partial Grams, simulated on this GPU: one
+        // workgroup per row of each view (pack) or of each matrix (reduce)
+        int64_t t = 0;
+        for (size_t s = 0; s < ch.segs.size(); ++s) {
+          ga.seg[s].tiles_per_view = int32_t(ch.segs[s].mp);
+          ga.seg[s].tile_begin = int32_t(t);
+          t += ch.segs[s].mp * ch.segs[s].count;
+        }
+        e = timed(kTReduce, st, [&] { return launch_tri_pack(ga, bf16, st); });
+        if (e != hipSuccess) return hip_fail(e, "triangle pack launch");
+        t = 0;
+        for (size_t s = 0; s < ch.segs.size(); ++s) {
+          const int64_t tt = ch.segs[s].mp / 64;
+          ga.seg[s].tiles_per_view = int32_t(tt * (tt + 1) / 2);
+          ga.seg[s].tile_begin = int32_t(t);
+          t += ga.seg[s].tiles_per_view * (ch.segs[s].count / ga.group);
+        }
+        e = timed(kTReduce, st, [&] { return launch_tri_reduce(ga, bf16, st); });
+        if (e != hipSuccess) return hip_fail(e, "triangle reduce launch");
+        set_tiles(true);
+      }
       e = timed(kTAA, st, [&] { return launch_gemm(ga, kAA, bf16, st); });
       if (e != hipSuccess) return hip_fail(e, "A*A launch");
       set_tiles(false);
@@ -365,7 +391,7 @@ muon_status muon_set_phase_timing(int32_t enable) {
   return ok();
 }
 
-muon_status muon_phase_times(double ms[7], int64_t launches[7]) {
+muon_status muon_phase_times(double ms[8], int64_t launches[8]) {
   double acc[kTKinds] = {};
   int64_t cnt[kTKinds] = {};
   for (size_t i = 0; i < g_timing.kinds.size(); ++i) {

@@ -57,7 +57,7 @@ struct ElemArgs {
 struct GemmSeg {
   char *base;
   int64_t stride;
-  int64_t off_xa[2], off_ahi, off_alo, off_b, off_bdiag, off_part, off_scale;
+  int64_t off_xa[2], off_ahi, off_alo, off_b, off_bdiag, off_part, off_scale, off_tri;
   int32_t mp, np;
   int32_t count;
   int32_t tiles_per_view;
@@ -79,6 +79,9 @@ struct GemmArgs {
   int32_t remap;    // XCD-aware tile order
   int32_t persistent; // > 0: grid of this many workgroups (a multiple of 8),
                       // each looping over tiles of its XCD's range
+  int32_t group;      // views per matrix that share one norm and one Gram
+                      // (distributed mode: the shards), else 1
+  int32_t gram_halves;// bf16 Gram: 1 writes A hi only, 2 also A lo
   float a, b, c;
   float r;          // b / c: the A*A kernel adds r A inside its K loop, then scales by c
   float eps;
@@ -113,5 +116,13 @@ hipError_t launch_elem(const ElemArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_norm_finalize(const GemmArgs &a, int views, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &a, int phase, bool bf16, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs &a, bool bf16, hipStream_t s);
+// Distributed mode (dist.hip): pack each shard's Gram into its upper-triangle
+// buffer (tiles_per_view = mp: one workgroup per row of a view); sum the
+// packed buffers of every matrix's shards in shard order and unpack the sum
+// into every shard's A (tiles_per_view = t (t + 1) / 2 upper 64 x 64 tiles
+// per matrix, t = mp / 64, with count / group matrices per segment).
+// tile_begin holds the prefix over segments in both cases.
+hipError_t launch_tri_pack(const GemmArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_tri_reduce(const GemmArgs &a, bool bf16, hipStream_t s);
 
 }  // namespace muon

@@ -233,26 +233,29 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
 }
 
 // s = 1 / (||X0||_F + eps) from the per-tile partial sums, summed in a fixed
-// order in double precision. One workgroup per view.
+// order in double precision. One workgroup per matrix: its `group`
+// consecutive views (1, or the shards of a distributed matrix, whose norm is
+// that of the whole matrix) all receive the same scale.
 __global__ __launch_bounds__(256) void norm_finalize_kernel(const GemmArgs args) {
   __shared__ double red[256];
-  const int vg = blockIdx.x, tid = threadIdx.x;
+  const int vg = int(blockIdx.x) * args.group, tid = threadIdx.x;
   int s = 0;
   while (s + 1 < args.nseg && vg >= args.seg[s + 1].view_begin) ++s;
   const GemmSeg &S = args.seg[s];
-  char *blk = S.base + int64_t(vg - S.view_begin) * S.stride;
-  const float *part = reinterpret_cast<const float *>(blk + S.off_part);
   double acc = 0.0;
-  for (int i = tid; i < S.nparts; i += 256) acc += double(part[i]);
+  for (int g = 0; g < args.group; ++g) {
+    const float *part = reinterpret_cast<const float *>(S.base + int64_t(vg + g - S.view_begin) * S.stride + S.off_part);
+    for (int i = tid; i < S.nparts; i += 256) acc += double(part[i]);
+  }
   red[tid] = acc;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
-  if (tid == 0) {
+  if (tid < args.group) {
     const double sc = 1.0 / (sqrt(red[0]) + double(args.eps));
-    float *scale = reinterpret_cast<float *>(blk + S.off_scale);
+    float *scale = reinterpret_cast<float *>(S.base + int64_t(vg + tid - S.view_begin) * S.stride + S.off_scale);
     scale[0] = float(sc);
     scale[1] = float(sc * sc);
   }
@@ -755,8 +758,9 @@ void gemm_bf16_kernel(const GemmArgs args) {
         a[r] = __uint_as_float(pack_bf16(x, x - float(bf16(x))));
       }
     });
-    // (the lo half is not needed when A*A runs on bf16(A) alone)
-    const int halves = args.aa_plain ? 1 : 2;
+    // (the lo half is not needed when A*A runs on bf16(A) alone, unless the
+    // Gram is a shard's partial that goes into a sum)
+    const int halves = args.gram_halves;
     for (int half = 0; half < halves; ++half) {  // 0: hi (bits 16..31), 1: lo
       bf16 *dst = reinterpret_cast<bf16 *>(blk + (half ? S.off_alo : S.off_ahi));
       const int shift = half ? 0 : 16;
@@ -944,7 +948,7 @@ hipError_t launch_elem(const ElemArgs &a, bool bf16, hipStream_t s) {
 
 hipError_t launch_norm_finalize(const GemmArgs &a, int views, hipStream_t s) {
   if (views <= 0) return hipSuccess;
-  hipLaunchKernelGGL(norm_finalize_kernel, dim3(views), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(views / a.group), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

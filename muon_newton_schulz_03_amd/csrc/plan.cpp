@@ -31,7 +31,7 @@ size_t dtype_size(int32_t dtype) {
   }
 }
 
-Layout view_layout(int64_t mp, int64_t np, bool bf16) {
+Layout view_layout(int64_t mp, int64_t np, bool bf16, bool distributed) {
   const size_t es = bf16 ? 2 : 4;
   const size_t mn = size_t(mp) * size_t(np) * es;
   const size_t mm = size_t(mp) * size_t(mp) * es;
@@ -54,13 +54,17 @@ Layout view_layout(int64_t mp, int64_t np, bool bf16) {
   off = align_up(off + size_t(L.nparts) * sizeof(float), 256);
   L.scale = off;
   off = align_up(off + 4 * sizeof(float), 256);
+  L.tri = off;
+  if (distributed) off = align_up(off + size_t(mp) * size_t(mp + 1) / 2 * sizeof(float), 256);
   L.total = off;
   return L;
 }
 
 bool validate_mode(uint32_t mode, Error *err) {
-  const uint32_t known = MUON_NS_BLOCKWISE | MUON_PACK_COST | MUON_AA_SPLIT;
+  const uint32_t known = MUON_NS_BLOCKWISE | MUON_NS_DISTRIBUTED | MUON_PACK_COST | MUON_AA_SPLIT;
   if (mode & ~known) return err->set(MUON_ERR_INVALID_ARG, fmt("unknown mode bits 0x%llx", mode & ~known));
+  if ((mode & MUON_NS_BLOCKWISE) && (mode & MUON_NS_DISTRIBUTED))
+    return err->set(MUON_ERR_INVALID_ARG, "MUON_NS_BLOCKWISE and MUON_NS_DISTRIBUTED exclude each other");
   return true;
 }
 
@@ -68,6 +72,7 @@ bool validate_descs(const muon_mat *d, int32_t n, uint32_t mode, const char *wha
   if (n < 0 || n > kMaxMats) return err->set(MUON_ERR_INVALID_ARG, fmt("n_mats %lld out of range", n));
   if (n > 0 && !d) return err->set(MUON_ERR_INVALID_ARG, std::string(what) + " is NULL");
   const bool blockwise = mode & MUON_NS_BLOCKWISE;
+  const bool distributed = mode & MUON_NS_DISTRIBUTED;
   for (int32_t i = 0; i < n; ++i) {
     const muon_mat &x = d[i];
     const std::string who = std::string(what) + fmt("[%lld]", i);
@@ -78,10 +83,16 @@ bool validate_descs(const muon_mat *d, int32_t n, uint32_t mode, const char *wha
     if (x.rows <= 0 || x.cols <= 0) return err->set(MUON_ERR_SHAPE, who + fmt(": rows %lld, cols %lld must be positive", x.rows, x.cols));
     if (x.ld < x.cols) return err->set(MUON_ERR_SHAPE, who + fmt(": ld %lld < cols %lld", x.ld, x.cols));
     if (x.col_blocks < 0) return err->set(MUON_ERR_SHAPE, who + ": col_blocks < 0");
-    int64_t k = (blockwise && x.col_blocks > 1) ? x.col_blocks : 1;
+    int64_t k = ((blockwise || distributed) && x.col_blocks > 1) ? x.col_blocks : 1;
     if (x.cols % k) return err->set(MUON_ERR_SHAPE, who + fmt(": col_blocks %lld does not divide cols %lld", k, x.cols));
+    if (distributed && std::max<int32_t>(x.col_blocks, 1) != std::max<int32_t>(d[0].col_blocks, 1))
+      return err->set(MUON_ERR_SHAPE, who + ": distributed mode needs the same col_blocks (shard count) for every matrix");
+    if (distributed && x.rows > x.cols)
+      return err->set(MUON_ERR_SHAPE, who + ": distributed mode shards the long side of a wide matrix; "
+                                            "pass a tall matrix transposed (rows <= cols)");
     const int64_t bc = x.cols / k;
-    const int64_t lo = std::min<int64_t>(x.rows, bc), hi = std::max<int64_t>(x.rows, bc);
+    const int64_t lo = distributed ? x.rows : std::min<int64_t>(x.rows, bc);
+    const int64_t hi = distributed ? bc : std::max<int64_t>(x.rows, bc);
     if (lo > kMaxMinDim || hi > kMaxMaxDim)
       return err->set(MUON_ERR_SHAPE, who + fmt(": shape %lld x %lld beyond the supported maximum", x.rows, bc));
     if (x.ld > (int64_t(1) << 40) / int64_t(es)) return err->set(MUON_ERR_SHAPE, who + ": ld too large");
@@ -165,8 +176,18 @@ bool build_plan(const muon_mat *d, int32_t n, int32_t iters, uint32_t mode, size
   p.bf16 = n > 0 ? d[0].dtype == MUON_BF16 : true;
   p.pad = p.bf16 ? kPadBf16 : kPadF32;
   const bool blockwise = mode & MUON_NS_BLOCKWISE;
+  p.distributed = mode & MUON_NS_DISTRIBUTED;
+  if (p.distributed) {
+    // every matrix must have the same shard count: the all-reduce of a
+    // launch sums a fixed number of consecutive views
+    p.shards = n > 0 ? std::max<int32_t>(d[0].col_blocks, 1) : 1;
+    for (int32_t i = 0; i < n; ++i)
+      if (std::max<int32_t>(d[i].col_blocks, 1) != p.shards)
+        return err->set(MUON_ERR_SHAPE, fmt("distributed mode: matrix %lld has col_blocks %lld, matrix 0 has %lld",
+                                            i, int64_t(d[i].col_blocks), int64_t(p.shards)));
+  }
   for (int32_t i = 0; i < n; ++i) {
-    const int64_t k = (blockwise && d[i].col_blocks > 1) ? d[i].col_blocks : 1;
+    const int64_t k = ((blockwise || p.distributed) && d[i].col_blocks > 1) ? d[i].col_blocks : 1;
     const int64_t bc = d[i].cols / k;
     for (int64_t b = 0; b < k; ++b) {
       View v;
@@ -175,14 +196,16 @@ bool build_plan(const muon_mat *d, int32_t n, int32_t iters, uint32_t mode, size
       v.rows = d[i].rows;
       v.cols = bc;
       v.col_off = b * bc;
-      v.tall = v.rows > v.cols;
-      v.m = std::min(v.rows, v.cols);
-      v.n = std::max(v.rows, v.cols);
+      // a shard keeps the orientation of its (wide) matrix: X_p is m x n/P
+      // even when n/P < m, so that sum_p X_p X_p^T is the Gram of X
+      v.tall = p.distributed ? false : v.rows > v.cols;
+      v.m = p.distributed ? v.rows : std::min(v.rows, v.cols);
+      v.n = p.distributed ? v.cols : std::max(v.rows, v.cols);
       v.mp = round_up(v.m, p.pad);
       v.np = round_up(v.n, p.pad);
       const double m = double(v.m), nn = double(v.n);
       v.cost = double(std::max(iters, 1)) * (4.0 * m * m * nn + 2.0 * m * m * m);
-      v.bytes = view_layout(v.mp, v.np, p.bf16).total;
+      v.bytes = view_layout(v.mp, v.np, p.bf16, p.distributed).total;
       p.views.push_back(v);
     }
   }
@@ -190,7 +213,7 @@ bool build_plan(const muon_mat *d, int32_t n, int32_t iters, uint32_t mode, size
     std::stable_sort(p.views.begin(), p.views.end(), [](const View &a, const View &b) { return a.cost > b.cost; });
   for (const View &v : p.views) {
     p.full_bytes += v.bytes;
-    p.min_bytes = std::max(p.min_bytes, v.bytes);
+    p.min_bytes = std::max(p.min_bytes, v.bytes * size_t(p.shards));  // a matrix's shards go together
   }
   const size_t cap = ws_bytes ? ws_bytes : p.full_bytes;
   if (!p.views.empty() && cap < p.min_bytes)
@@ -205,7 +228,12 @@ bool build_plan(const muon_mat *d, int32_t n, int32_t iters, uint32_t mode, size
     const View &v = p.views[vi];
     const bool same_shape = !cur.segs.empty() && cur.segs.back().mp == v.mp && cur.segs.back().np == v.np;
     const bool need_seg = !same_shape;
-    if (cur.count && (cur.bytes + v.bytes > cap || (need_seg && int(cur.segs.size()) == kMaxSegs))) flush();
+    // a group starts only at a matrix boundary in distributed mode (the
+    // shards of one matrix share their Gram and must be in flight together)
+    const bool boundary = !p.distributed || v.block == 0;
+    const size_t need = v.bytes * size_t(p.distributed ? p.shards : 1);
+    if (boundary && cur.count && (cur.bytes + need > cap || (need_seg && int(cur.segs.size()) == kMaxSegs)))
+      flush();
     if (!cur.count) cur.first = vi;
     if (cur.segs.empty() || !(cur.segs.back().mp == v.mp && cur.segs.back().np == v.np)) {
       Segment s;
@@ -236,7 +264,8 @@ bool build_plan(const muon_mat *d, int32_t n, int32_t iters, uint32_t mode, size
 
 std::string plan_json(const Plan &p) {
   std::ostringstream o;
-  o << "{\"bf16\":" << (p.bf16 ? "true" : "false") << ",\"pad\":" << p.pad << ",\"iters\":" << p.iters
+  o << "{\"bf16\":" << (p.bf16 ? "true" : "false") << ",\"distributed\":" << (p.distributed ? "true" : "false")
+    << ",\"shards\":" << p.shards << ",\"pad\":" << p.pad << ",\"iters\":" << p.iters
     << ",\"mode\":" << p.mode << ",\"full_bytes\":" << p.full_bytes << ",\"min_bytes\":" << p.min_bytes
     << ",\"views\":[";
   for (size_t i = 0; i < p.views.size(); ++i) {
@@ -259,10 +288,10 @@ std::string plan_json(const Plan &p) {
       o << "{\"first\":" << sg.first << ",\"count\":" << sg.count << ",\"mp\":" << sg.mp << ",\"np\":" << sg.np
         << ",\"base\":" << sg.base << ",\"stride\":" << sg.stride << ",\"tiles_syrk\":" << sg.tiles_syrk
         << ",\"tiles_gemm\":" << sg.tiles_gemm;
-      const Layout L = view_layout(sg.mp, sg.np, p.bf16);
+      const Layout L = view_layout(sg.mp, sg.np, p.bf16, p.distributed);
       o << ",\"layout\":{\"xa\":[" << L.xa[0] << "," << L.xa[1]
         << "],\"ahi\":" << L.ahi << ",\"alo\":" << L.alo << ",\"b\":" << L.b << ",\"bdiag\":" << L.bdiag
-        << ",\"partials\":" << L.partials
+        << ",\"partials\":" << L.partials << ",\"tri\":" << L.tri
         << ",\"scale\":" << L.scale << ",\"total\":" << L.total << "}}";
       ts += sg.tiles_syrk * sg.count;
       tg += sg.tiles_gemm * sg.count;

@@ -36,14 +36,16 @@ struct Layout {
   size_t bdiag;     // bf16 path: diagonal of B in float32
   size_t partials;  // per-64x64-tile sums of squares (float)
   size_t scale;     // s = 1/(||X||_F + eps), s^2 (float)
+  size_t tri;       // distributed mode: this shard's Gram, upper triangle packed
+                    // row by row as float32 (mp (mp + 1) / 2 entries)
   size_t total;
   int64_t nparts;
 };
 
-Layout view_layout(int64_t mp, int64_t np, bool bf16);
+Layout view_layout(int64_t mp, int64_t np, bool bf16, bool distributed = false);
 
 struct View {
-  int32_t mat = 0, block = 0;
+  int32_t mat = 0, block = 0;  // block: column block (blockwise) or shard (distributed)
   int64_t rows = 0, cols = 0;  // user orientation
   int64_t col_off = 0;         // first column of the block inside the matrix
   bool tall = false;
@@ -69,6 +71,8 @@ struct Chunk {
 
 struct Plan {
   bool bf16 = true;
+  bool distributed = false;
+  int32_t shards = 1;  // distributed mode: views per matrix, consecutive in every chunk
   int pad = kPadBf16;
   int iters = 5;
   uint32_t mode = 0;

@@ -14,6 +14,7 @@ from .muon_oracle import (  # noqa: F401
     frobenius_normalize,
     newton_schulz,
     newton_schulz_blockwise,
+    newton_schulz_distributed,
     muon_step,
     newton_schulz_iteration_rows,
 )

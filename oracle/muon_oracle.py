@@ -137,6 +137,35 @@ def newton_schulz_blockwise(X, col_blocks, iters=5, coeffs=DEFAULT_COEFFS,
     return np.concatenate(parts, axis=1)
 
 
+def newton_schulz_distributed(X, shards, iters=5, coeffs=DEFAULT_COEFFS,
+                              eps=DEFAULT_EPS, dtype=np.float64):
+    """Distributed (tensor-parallel) mode: the wide matrix X is split by
+    columns into ``shards`` pieces X_p, as P GPUs would hold it ([zh]
+    "Distributed mode"; [pt] "2. Newton-Schulz distribuído"). Each iteration
+    sums the shards' partial Grams X_p X_p^T in shard order (the all-reduce
+    after the first product), forms B from the full A on every shard, and
+    updates each shard with its own columns: X_p <- a X_p + B X_p. The norm is
+    that of the whole matrix (sum of the shards' squared norms). The result
+    equals ``newton_schulz(X)`` up to rounding order; X must be wide
+    (rows <= cols) and ``shards`` must divide its column count."""
+    X = np.array(X, dtype=dtype)
+    rows, cols = X.shape
+    if rows > cols or shards < 1 or cols % shards:
+        raise ValueError("distributed mode needs a wide matrix and equal column shards")
+    a, b, c = (dtype(v) for v in coeffs)
+    w = cols // shards
+    parts = [X[:, p * w:(p + 1) * w] for p in range(shards)]
+    nrm = np.sqrt(sum(np.sum(P * P) for P in parts))
+    parts = [P / (nrm + eps) for P in parts]
+    for _ in range(iters):
+        A = np.zeros((rows, rows), dtype=dtype)
+        for P in parts:
+            A = A + P @ P.T
+        B = b * A + c * (A @ A)
+        parts = [a * P + B @ P for P in parts]
+    return np.concatenate(parts, axis=1)
+
+
 def muon_step(W, G, M, lr, beta, nesterov=False, iters=5,
               coeffs=DEFAULT_COEFFS, eps=DEFAULT_EPS, col_blocks=1,
               dtype=np.float64):

@@ -55,7 +55,14 @@ def test_ns_validation_codes(lib):
     assert call([desc(4, 8)], n=-1) == mu.MUON_ERR_INVALID_ARG
     assert call([desc(4, 8)], iters=-1) == mu.MUON_ERR_INVALID_ARG
     assert call([desc(4, 8)], iters=65) == mu.MUON_ERR_INVALID_ARG
-    assert call([desc(4, 8)], mode=0x2) == mu.MUON_ERR_INVALID_ARG
+    assert call([desc(4, 8)], mode=0x4) == mu.MUON_ERR_INVALID_ARG
+    both = mu.MUON_NS_BLOCKWISE | mu.MUON_NS_DISTRIBUTED
+    assert call([desc(4, 8, col_blocks=2)], mode=both) == mu.MUON_ERR_INVALID_ARG
+    dist = mu.MUON_NS_DISTRIBUTED
+    assert call([desc(9, 8, col_blocks=2)], mode=dist) == mu.MUON_ERR_SHAPE      # tall
+    assert call([desc(4, 9, col_blocks=2)], mode=dist) == mu.MUON_ERR_SHAPE      # 2 does not divide 9
+    assert call([desc(4, 8, col_blocks=2), desc(4, 8, col_blocks=4, ptr=FAKE * 2)],
+                mode=dist) == mu.MUON_ERR_SHAPE                                    # unequal shard counts
     assert call([desc(4, 8, ptr=0)]) == mu.MUON_ERR_INVALID_ARG
     assert call([desc(0, 8)]) == mu.MUON_ERR_SHAPE
     assert call([desc(4, -1)]) == mu.MUON_ERR_SHAPE
@@ -230,6 +237,30 @@ def test_plan_blockwise_expansion():
     assert all(x["tall"] and (x["m"], x["n"]) == (2304, 7168) for x in v)
     # without the blockwise bit col_blocks is ignored
     assert len(mu.muon_plan_info(ds)["views"]) == 1
+
+
+def test_plan_distributed_shards():
+    """Distributed mode: P shards per matrix, each m x n/P in the matrix's
+    own orientation (even when n/P < m), consecutive, never split across
+    groups, with a packed-triangle buffer of mp (mp + 1) / 2 floats."""
+    ds = [desc(300, 1000, col_blocks=4), desc(200, 400, col_blocks=4, ptr=FAKE * 2),
+          desc(300, 1000, col_blocks=4, ptr=FAKE * 3)]
+    p = mu.muon_plan_info(ds, mode=mu.MUON_NS_DISTRIBUTED | mu.MUON_PACK_COST)
+    assert p["distributed"] and p["shards"] == 4
+    v = p["views"]
+    assert len(v) == 12
+    for k in range(0, 12, 4):
+        assert [x["block"] for x in v[k:k + 4]] == [0, 1, 2, 3]
+        assert len({x["mat"] for x in v[k:k + 4]}) == 1
+    first = v[0]
+    assert (first["m"], first["n"], first["tall"]) == (300, 250, False)
+    L = p["chunks"][0]["segments"][0]["layout"]
+    mp = p["chunks"][0]["segments"][0]["mp"]
+    assert L["total"] - L["tri"] >= mp * (mp + 1) // 2 * 4
+    # a workspace of one matrix's shards: one matrix per group
+    one = 4 * v[0]["bytes"]
+    q = mu.muon_plan_info(ds, mode=mu.MUON_NS_DISTRIBUTED | mu.MUON_PACK_COST, workspace_bytes=one)
+    assert [c["count"] for c in q["chunks"]] == [4, 4, 4]
 
 
 def test_plan_layout_disjoint():

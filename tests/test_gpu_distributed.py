@@ -1,0 +1,103 @@
+"""GPU parity of the distributed (column-sharded) mode simulated on one GPU,
+through the C ABI: the result against the float64 oracle of the whole matrix
+(which the sharded computation must equal up to rounding order), the packed
+upper-triangle partial Grams each shard would send, and the summed Gram every
+shard receives."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import np64, padded, relF
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+def rand(shape, dtype, seed, std=0.01):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    _, v = padded(shape[0], shape[1], dtype)
+    v.copy_(torch.randn(shape, generator=g, device="cuda") * std)
+    return v
+
+
+@pytest.mark.parametrize("shape,shards", [((256, 1024), 1), ((256, 1024), 4), ((300, 1000), 4),
+                                          ((512, 512), 4), ((128, 2048), 8)])
+def test_distributed_bf16_matches_whole_matrix(gpu_lib, shape, shards):
+    import muon_newton_schulz_03_amd as mu
+    X = rand(shape, torch.bfloat16, 21 + shards)
+    X0 = np64(X)
+    ref = oracle.newton_schulz(X0)
+    assert relF(oracle.newton_schulz_distributed(X0, shards), ref) < 1e-12
+    Y = X.clone()
+    gpu_lib.muon_ns_batched([Y], iters=5, mode=mu.MUON_NS_DISTRIBUTED, col_blocks=shards)
+    torch.cuda.synchronize()
+    err = relF(np64(Y), ref)
+    print(f"{shape} x{shards} shards: relF {err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_distributed_f32(gpu_lib):
+    import muon_newton_schulz_03_amd as mu
+    X = rand((64, 384), torch.float32, 5, std=1.0)
+    X0 = np64(X)
+    gpu_lib.muon_ns_batched([X], iters=5, mode=mu.MUON_NS_DISTRIBUTED, col_blocks=3)
+    torch.cuda.synchronize()
+    assert relF(np64(X), oracle.newton_schulz(X0)) <= F32_TOL
+
+
+def test_distributed_batch_and_step(gpu_lib):
+    """Several matrices (grouped launches, cost order) and the full Muon step."""
+    import muon_newton_schulz_03_amd as mu
+    shapes = [(256, 1024), (128, 512), (256, 1024), (64, 1024)]
+    W = [rand(s, torch.bfloat16, 40 + i, std=0.02) for i, s in enumerate(shapes)]
+    G = [rand(s, torch.bfloat16, 50 + i, std=1e-3) for i, s in enumerate(shapes)]
+    M = [rand(s, torch.bfloat16, 60 + i, std=1e-2) for i, s in enumerate(shapes)]
+    W0, G0, M0 = [np64(t) for t in W], [np64(t) for t in G], [np64(t) for t in M]
+    Wz = [torch.zeros_like(t) for t in W]
+    gpu_lib.muon_step(Wz, G, M, lr=-1.0, beta=float(np.float32(0.95)),
+                      mode=mu.MUON_NS_DISTRIBUTED | mu.MUON_PACK_COST, col_blocks=4)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        O_ref, _, _ = oracle.muon_step(W0[i], G0[i], M0[i], lr=0.0, beta=float(np.float32(0.95)))
+        assert relF(np64(Wz[i]), O_ref) <= BF16_TOL
+
+
+def test_packed_partial_grams(gpu_lib):
+    """After one iteration each shard's packed buffer holds its partial Gram
+    s^2 X_p X_p^T (upper triangle, row i from column i), and every shard's A
+    is the sum, bitwise identical across shards and symmetric."""
+    import muon_newton_schulz_03_amd as mu
+    shape, P = (300, 1000), 4
+    X = rand(shape, torch.bfloat16, 7)
+    X0 = np64(X)
+    mode = mu.MUON_NS_DISTRIBUTED | mu.MUON_PACK_RR
+    gpu_lib.muon_ns_batched([X], iters=1, mode=mode, col_blocks=P)
+    torch.cuda.synchronize()
+    desc = mu.mat_of(X, P)
+    plan = mu.muon_plan_info([desc], iters=1, mode=mode, workspace_bytes=mu._ws.nbytes)
+    seg = plan["chunks"][0]["segments"][0]
+    L, mp, stride, base = seg["layout"], seg["mp"], seg["stride"], seg["base"]
+    buf = mu._ws.buf
+    m, w = shape[0], shape[1] // P
+    s = 1.0 / (np.linalg.norm(X0) + 1e-7)
+    iu = np.triu_indices(mp)
+    As = []
+    for p in range(P):
+        blk = base + p * stride
+        tri = buf[blk + L["tri"]: blk + L["tri"] + mp * (mp + 1) // 2 * 4].view(torch.float32).cpu().numpy()
+        Xp = np.zeros((mp, w))
+        Xp[:m] = X0[:, p * w:(p + 1) * w]
+        part = s * s * (Xp @ Xp.T)
+        assert relF(tri.astype(np.float64), part[iu]) < 1e-4
+        Ah = buf[blk + L["ahi"]: blk + L["ahi"] + mp * mp * 2].view(torch.bfloat16).view(mp, mp)
+        Al = buf[blk + L["alo"]: blk + L["alo"] + mp * mp * 2].view(torch.bfloat16).view(mp, mp)
+        As.append((Ah.clone(), Al.clone()))
+    for Ah, Al in As:
+        assert torch.equal(Ah, As[0][0]) and torch.equal(Al, As[0][1])
+        assert torch.equal(Ah, Ah.t())
+    A = np64(As[0][0]) + np64(As[0][1])
+    assert relF(A[:m, :m], s * s * (X0 @ X0.T)) < 1e-4

@@ -372,3 +372,55 @@ def test_pins_catch_planted_mistake(old, new):
     ns_ns = dict(vars(om))
     exec(compile(src.replace(old, new), "<mutant>", "exec"), ns_ns)
     assert not _pins_pass(ns_ns["newton_schulz"])
+
+
+# ---------------------------------------------------------------------------
+# distributed (column-sharded) mode: the sum of the shards' partial Grams is
+# the Gram of the whole matrix, so the result must be the full-matrix one
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,shards", [((12, 40), 1), ((12, 40), 4), ((16, 48), 8), ((20, 20), 5)])
+def test_distributed_equals_full(shape, shards):
+    X = np.random.default_rng(11).standard_normal(shape)
+    full = oracle.newton_schulz(X)
+    dist = oracle.newton_schulz_distributed(X, shards)
+    assert relF(dist, full) < 1e-13
+    assert relF(dist, closed_form(X, 5)) < 1e-12
+
+
+def test_distributed_is_not_blockwise():
+    """With several shards the shared Gram makes the result differ from
+    orthogonalizing each column block alone."""
+    X = np.random.default_rng(12).standard_normal((12, 48))
+    assert relF(oracle.newton_schulz_distributed(X, 4), oracle.newton_schulz_blockwise(X, 4)) > 1e-2
+
+
+def test_distributed_rejects_tall_and_ragged():
+    with pytest.raises(ValueError):
+        oracle.newton_schulz_distributed(np.ones((8, 4)), 2)
+    with pytest.raises(ValueError):
+        oracle.newton_schulz_distributed(np.ones((4, 9)), 2)
+
+
+DIST_MUTATIONS = [
+    ("            A = A + P @ P.T", "            A = P @ P.T"),
+    ("    nrm = np.sqrt(sum(np.sum(P * P) for P in parts))", "    nrm = np.sqrt(np.sum(parts[0] * parts[0]))"),
+    ("        parts = [a * P + B @ P for P in parts]", "        parts = [a * P + B @ P.T.T * 0 + B @ parts[0] * 0 + B @ P * (P is parts[0]) for P in parts]"),
+]
+
+
+@pytest.mark.parametrize("old,new", DIST_MUTATIONS)
+def test_distributed_pins_catch_planted_mistake(old, new):
+    import inspect
+    from oracle import muon_oracle
+    src = inspect.getsource(muon_oracle.newton_schulz_distributed)
+    assert old in src
+    ns = dict(vars(muon_oracle))
+    exec(src.replace(old, new), ns)
+    orig = oracle.newton_schulz_distributed
+    oracle.newton_schulz_distributed = ns["newton_schulz_distributed"]
+    try:
+        with pytest.raises(AssertionError):
+            test_distributed_equals_full((16, 48), 8)
+    finally:
+        oracle.newton_schulz_distributed = orig

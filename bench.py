@@ -309,9 +309,8 @@ def main():
             "flops_per_launch": fl_launch,
             "avg_launch_ms": round(avg_ms, 4),
         }
-        el_bytes = acc.elementwise_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4)
-        el_ms = per_step["prep"][0] + per_step["finish"][0]
-        out["elementwise_gbs"] = round(el_bytes / (el_ms * 1e-3) / 1e9, 1) if el_ms > 0 else None
+        pb = acc.prep_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4)
+        out["prep_gbs"] = round(pb / (per_step["prep"][0] * 1e-3) / 1e9, 1) if per_step["prep"][0] > 0 else None
     if args.tp > 0 and phases:
         P = args.tp
         red = per_step.get("reduce", (0.0, 0))[0]

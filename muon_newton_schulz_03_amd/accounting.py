@@ -73,3 +73,10 @@ def elementwise_bytes(shapes, elem_size):
     """Algorithmic HBM bytes of momentum + update for one step."""
     n = sum(r * c for (r, c) in shapes)
     return 6 * n * elem_size
+
+
+def prep_bytes(shapes, elem_size):
+    """HBM bytes of the prep pass: read G and M, write M and the
+    Newton-Schulz source X0 (the update itself runs inside the last B X)."""
+    n = sum(r * c for (r, c) in shapes)
+    return 4 * n * elem_size

@@ -268,14 +268,20 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       if (e != hipSuccess) return hip_fail(e, "A*A launch");
       set_tiles(false);
       // B X (short K loop): persistent workgroups, so that a tile's epilogue
-      // stores overlap the next tile's first operand loads
+      // stores overlap the next tile's first operand loads. The last one
+      // writes the caller's matrices (data <- O or W <- W - lr O).
       ga.persistent = (slots > 0 && ga.total_tiles > slots) ? slots : 0;
+      ga.last = it == iters - 1 ? 1 : 0;
+      ga.lr = lr;
       e = timed(kTBX, st, [&] { return launch_gemm(ga, kBX, bf16, st); });
       ga.persistent = 0;
+      ga.last = 0;
       if (e != hipSuccess) return hip_fail(e, "B*X launch");
     }
-    s = elem_pass(false);
-    if (s != MUON_OK) return s;
+    if (iters == 0) {  // nothing to fuse with: write back the normalized source
+      s = elem_pass(false);
+      if (s != MUON_OK) return s;
+    }
   }
   return ok();
 }

@@ -44,6 +44,21 @@ struct ElemView {
   int32_t pad_;
 };
 
+// Where the result of a view goes, recorded by the prep kernel in the view's
+// workspace block (kOutDescOffset bytes into its scale region) and read by
+// the last B X, which then writes the caller's matrix itself: data <- O
+// (muon_ns_batched) or W <- W - lr O (muon_step), in the user's orientation.
+struct OutDesc {
+  void *out;       // caller's matrix at the view's first column (W, or the data)
+  int64_t ld;      // its row pitch (elements)
+  int32_t rows, cols;  // view shape in the user's orientation
+  int32_t tall;    // the user's view is X^T (wide X = user transposed)
+  int32_t update;  // 1: W <- W - lr O; 0: out <- O
+  int32_t vec;     // rows start on 8-byte boundaries (4-element runs)
+  int32_t pad_;
+};
+constexpr int kOutDescOffset = 64;
+
 struct ElemArgs {
   ElemView v[kElemViewsMax];
   int32_t nv;
@@ -79,6 +94,9 @@ struct GemmArgs {
   int32_t remap;    // XCD-aware tile order
   int32_t persistent; // > 0: grid of this many workgroups (a multiple of 8),
                       // each looping over tiles of its XCD's range
+  int32_t last;       // B X of the last iteration: write the caller's matrices
+                      // through each view's OutDesc instead of X'
+  float lr;           // muon_step's learning rate (for last)
   int32_t group;      // views per matrix that share one norm and one Gram
                       // (distributed mode: the shards), else 1
   int32_t gram_halves;// bf16 Gram: 1 writes A hi only, 2 also A lo

@@ -143,6 +143,18 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
 
   T *X = reinterpret_cast<T *>(Vw.blk + Vw.off_x);
   const int64_t px = Vw.pitch_x;
+  if ((kind == kPrepNs || kind == kPrepStep) && u == 0 && tid == 0) {
+    // where the last B X writes this view's result
+    OutDesc od{};
+    od.out = kind == kPrepStep ? Vw.w : Vw.m;
+    od.ld = kind == kPrepStep ? Vw.ld_w : Vw.ld_m;
+    od.rows = Vw.rows;
+    od.cols = Vw.cols;
+    od.tall = Vw.tall;
+    od.update = kind == kPrepStep ? 1 : 0;
+    od.vec = (reinterpret_cast<uintptr_t>(od.out) % 8 == 0 && (od.ld * int64_t(sizeof(T))) % 8 == 0) ? 1 : 0;
+    *reinterpret_cast<OutDesc *>(Vw.blk + Vw.off_scale + kOutDescOffset) = od;
+  }
   if (kind == kPrepNs || kind == kPrepStep) {
     // X0 in wide orientation: this tile's rows as they are, or (tall view)
     // transposed through the LDS tile
@@ -328,6 +340,53 @@ __device__ inline void tile_store(const char *smem, bf16 *dst, int64_t pitch, in
 __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
   __builtin_amdgcn_s_barrier();
+}
+
+// The last iteration's B X writes the caller's matrix itself: out <- O, or
+// W <- W - lr O with O rounded to bf16 first (bit for bit what a separate
+// pass reading X' back would produce). The LDS tile holds O in the user's
+// orientation (rows i for a wide view; rows j for a tall one, whose user
+// matrix is X^T); each thread then updates 16-byte runs of user rows,
+// skipping what lies outside the user's shape (padding).
+__device__ inline void tile_update_user(const char *smem, const OutDesc &od, float lr, int row0, int col0, int tid) {
+  const bool vec16 = reinterpret_cast<uintptr_t>(od.out) % 16 == 0 && (od.ld * 2) % 16 == 0;
+  // 16 runs per pass, their W loads all issued before the first is used
+  for (int k0 = 0; k0 < 32; k0 += 16) {
+    u32x4 w[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int u = tid + 256 * (k0 + k), ur = row0 + (u >> 5), uc = col0 + (u & 31) * 8;
+      w[k] = u32x4{0u, 0u, 0u, 0u};
+      if (od.update && vec16 && ur < od.rows && uc + 8 <= od.cols)
+        w[k] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(od.out) + int64_t(ur) * od.ld + uc);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int u = tid + 256 * (k0 + k), row = u >> 5, c = u & 31;
+      const int ur = row0 + row, uc = col0 + c * 8;
+      if (ur >= od.rows || uc >= od.cols) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + row * 512 + (tile_chunk(row, c) << 4));
+      bf16 *p = static_cast<bf16 *>(od.out) + int64_t(ur) * od.ld + uc;
+      if (vec16 && uc + 8 <= od.cols) {
+        u32x4 o = v;
+        if (od.update) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float r0 = fmaf(-lr, __uint_as_float(v[d] << 16), __uint_as_float(w[k][d] << 16));
+            const float r1 = fmaf(-lr, __uint_as_float(v[d] & 0xFFFF0000u), __uint_as_float(w[k][d] & 0xFFFF0000u));
+            o[d] = uint32_t(__builtin_bit_cast(uint16_t, bf16(r0))) | (uint32_t(__builtin_bit_cast(uint16_t, bf16(r1))) << 16);
+          }
+        }
+        *reinterpret_cast<u32x4 *>(p) = o;
+      } else {
+        for (int e = 0; e < 8 && uc + e < od.cols; ++e) {
+          bf16 x = __builtin_bit_cast(bf16, uint16_t((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+          if (od.update) x = bf16(fmaf(-lr, float(x), float(p[e])));
+          p[e] = x;
+        }
+      }
+    }
+  }
 }
 
 // Diagonal tile: the LDS tile holds L[c][r] = value computed at (r, c).
@@ -827,8 +886,19 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, sx * a[r]));
     });
-    store_direct(Y + int64_t(i0) * np + j0, np, acc, ec);
-    lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
+    if (args.last) {
+      const OutDesc od = *reinterpret_cast<const OutDesc *>(blk + S.off_scale + kOutDescOffset);
+      lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
+      if (od.tall)
+        fill_tile<true>(smem, acc, ec, 0);
+      else
+        fill_tile<false>(smem, acc, ec, 0);
+      lds_barrier();
+      tile_update_user(smem, od, args.lr, od.tall ? j0 : i0, od.tall ? i0 : j0, tid);
+    } else {
+      store_direct(Y + int64_t(i0) * np + j0, np, acc, ec);
+    }
+    lds_barrier();  // every wave is done with the LDS ring
   }
   }  // tiles of this workgroup
 }
@@ -925,12 +995,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs args) {
     const float sx = args.first ? reinterpret_cast<const float *>(blk + S.off_scale)[0] : 1.f;
     const float *X = reinterpret_cast<const float *>(blk + S.off_xa[args.src]);
     float *Ya = reinterpret_cast<float *>(blk + S.off_xa[args.src ^ 1]);
+    const OutDesc od = *reinterpret_cast<const OutDesc *>(blk + S.off_scale + kOutDescOffset);
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int i = i0 + ty + 16 * x, j = j0 + tx + 16 * y;
-        Ya[int64_t(i) * np + j] = sx * fmaf(args.a, X[int64_t(i) * np + j], acc[x][y]);
+        const float o = sx * fmaf(args.a, X[int64_t(i) * np + j], acc[x][y]);
+        if (!args.last) {
+          Ya[int64_t(i) * np + j] = o;
+        } else {
+          // the caller's matrix directly (see store_user)
+          const int ur = od.tall ? j : i, uc = od.tall ? i : j;
+          if (ur < od.rows && uc < od.cols) {
+            float *p = static_cast<float *>(od.out) + int64_t(ur) * od.ld + uc;
+            *p = od.update ? fmaf(-args.lr, o, *p) : o;
+          }
+        }
       }
   }
 }

@@ -140,7 +140,8 @@ def test_bf16_blockwise(gpu_lib, shape, k):
 def test_bf16_symmetric_intermediates(gpu_lib, split):
     """After one iteration the workspace holds A (hi, and lo in split mode)
     and B of it: bitwise symmetric (mirrored), A equal to s^2 X0 X0^T, zero
-    padding, B = b A + c A A with its diagonal in float32, and X1."""
+    padding, B = b A + c A A with its diagonal in float32, and X1 (in the
+    caller's matrix)."""
     import muon_newton_schulz_03_amd as mu
     shape = (300, 520)
     _, X = rand(shape, torch.bfloat16, 5, std=0.01)
@@ -181,11 +182,11 @@ def test_bf16_symmetric_intermediates(gpu_lib, split):
     print(f"B relF vs device A {relF(Bfull[:m, :m], Bdev[:m, :m]):.3e}, vs exact {relF(Bfull[:m, :m], Bref):.3e}")
     assert relF(Bfull[:m, :m], Bdev[:m, :m]) < 1e-2
     assert np.allclose(bdiag, np.diag(Bdev), rtol=1e-4, atol=1e-6)
-    X1 = np64(mat(L["xa"][1], mp, np_))
+    # the last B X writes X1 straight into the caller's matrix
+    X1 = np64(X)
     X1ref = s * (3.4445 * X0 + Bref @ X0)
-    print(f"X1 relF {relF(X1[:m, :shape[1]], X1ref):.3e}")
-    assert relF(X1[:m, :shape[1]], X1ref) < 1e-2
-    assert np.all(X1[m:, :] == 0) and np.all(X1[:, shape[1]:] == 0)
+    print(f"X1 relF {relF(X1, X1ref):.3e}")
+    assert relF(X1, X1ref) < 1e-2
 
 
 def test_bf16_deterministic_and_packing_invariant(gpu_lib):

@@ -6,11 +6,13 @@
 //                           orientation, per-tile partial sums of squares.
 //   norm_finalize_kernel    s = 1/(||X0||_F + eps) from the partial sums.
 //   iters x { gemm <Gram>   A = s' X X^T (upper-triangle tiles, mirrored),
-//                           stored as bf16 hi + lo;
+//                           stored as bf16 (hi, and lo when needed);
 //             gemm <AA>     B = b A + c A A (upper tiles, mirrored), A A from
-//                           hi*hi + hi*lo + lo*hi;
-//             gemm <BX>     X' = s'' (a X + B X) }
-//   elem_kernel (finish)    data <- O, or W <- W - lr O.
+//                           bf16(A), or from hi*hi + hi*lo + lo*hi;
+//             gemm <BX>     X' = s'' (a X + B X); the last one writes the
+//                           caller's matrix: data <- O, or W <- W - lr O }
+//   elem_kernel (finish)    only for zero iterations: data <- s X0, or
+//                           W <- W - lr s X0.
 // s' = s^2 and s'' = s in the first iteration (the normalization is folded
 // into the first Gram and the first B X), 1 afterwards.
 //

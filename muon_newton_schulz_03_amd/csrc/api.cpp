@@ -136,6 +136,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       g.base = ws + sg.base;
       g.stride = int64_t(sg.stride);
       for (int p = 0; p < 2; ++p) g.off_xa[p] = int64_t(L.xa[p]);
+      for (int p = 0; p < 2; ++p) g.off_xt[p] = int64_t(L.xt[p]);
       g.off_ahi = int64_t(L.ahi);
       g.off_alo = int64_t(L.alo);
       g.off_b = int64_t(L.b);
@@ -205,6 +206,9 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
         e.blk = blocks[k];
         const int buf = prep ? 0 : fin;
         e.off_x = int64_t(L.xa[buf]);
+        // X0^T too when a bf16 B X will read it
+        e.off_xt = (prep && bf16 && iters > 0) ? int64_t(L.xt[0]) : -1;
+        e.pitch_xt = int32_t(v.mp);
         e.off_part = int64_t(L.partials);
         e.off_scale = int64_t(L.scale);
         e.rows = int32_t(v.rows);

@@ -2,9 +2,10 @@
 //
 // Workspace: every view (a whole matrix, or a column block in blockwise mode)
 // owns one block of the caller's workspace holding X (wide orientation,
-// row-major, ping-pong), the Gram matrix A (bf16 hi/lo halves, or float32),
-// B = b A + c A A, the per-tile partial sums of squares and its scale
-// s = 1/(||X||_F + eps).
+// row-major, ping-pong), on the bf16 path also X^T (ping-pong: the right
+// operand of B X with k contiguous), the Gram matrix A (bf16 hi/lo halves,
+// or float32), B = b A + c A A, the per-tile partial sums of squares and its
+// scale s = 1/(||X||_F + eps).
 // Views of one padded shape sit at a uniform stride ("segment"), so a grouped
 // launch needs only a handful of segment descriptors in its kernel arguments.
 #pragma once
@@ -34,6 +35,7 @@ struct ElemView {
   int64_t ld_g, ld_m, ld_w;  // elements
   char *blk;                 // workspace block of the view
   int64_t off_x;             // X (wide orientation: X^T of the user's view if tall)
+  int64_t off_xt;            // prep: X^T as well (np x mp row-major), or -1
   int64_t off_part, off_scale;
   int32_t rows, cols;        // view shape, user orientation
   int32_t pitch_x;           // row pitch (elements) of X
@@ -41,7 +43,7 @@ struct ElemView {
   int32_t tiles_c;           // 64-wide tiles along the user's columns
   int32_t tile_begin;        // first tile of this view in the launch
   int32_t vec;               // bit 0/1/2: g/m/w rows start on 16-byte boundaries
-  int32_t pad_;
+  int32_t pitch_xt;          // row pitch (elements) of X^T
 };
 
 // Where the result of a view goes, recorded by the prep kernel in the view's
@@ -72,7 +74,7 @@ struct ElemArgs {
 struct GemmSeg {
   char *base;
   int64_t stride;
-  int64_t off_xa[2], off_ahi, off_alo, off_b, off_bdiag, off_part, off_scale, off_tri;
+  int64_t off_xa[2], off_xt[2], off_ahi, off_alo, off_b, off_bdiag, off_part, off_scale, off_tri;
   int32_t mp, np;
   int32_t count;
   int32_t tiles_per_view;
@@ -88,7 +90,7 @@ struct GemmArgs {
   GemmSeg seg[kSegsMax];
   int32_t nseg;
   int32_t total_tiles;
-  int32_t src;      // X buffer read this iteration; the product goes to src ^ 1
+  int32_t src;      // X (and X^T) buffer read this iteration; the product goes to src ^ 1
   int32_t first;    // first iteration: apply the normalization scale
   int32_t aa_plain; // A*A and b A from bf16(A) only (no lo half of A)
   int32_t remap;    // XCD-aware tile order

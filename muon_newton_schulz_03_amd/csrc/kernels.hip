@@ -3,14 +3,16 @@
 // Per group of views (whole matrices or column blocks), in stream order:
 //   elem_kernel (prep)      momentum M <- beta M + G, Newton-Schulz source X0
 //                           written zero-padded into the workspace in wide
-//                           orientation, per-tile partial sums of squares.
+//                           orientation (and transposed, X0^T, for the bf16
+//                           B X), per-tile partial sums of squares.
 //   norm_finalize_kernel    s = 1/(||X0||_F + eps) from the partial sums.
 //   iters x { gemm <Gram>   A = s' X X^T (upper-triangle tiles, mirrored),
 //                           stored as bf16 (hi, and lo when needed);
 //             gemm <AA>     B = b A + c A A (upper tiles, mirrored), A A from
 //                           bf16(A), or from hi*hi + hi*lo + lo*hi;
-//             gemm <BX>     X' = s'' (a X + B X); the last one writes the
-//                           caller's matrix: data <- O, or W <- W - lr O }
+//             gemm <BX>     X' = s'' (a X + B X), written as X' and X'^T;
+//                           the last one writes the caller's matrix instead:
+//                           data <- O, or W <- W - lr O }
 //   elem_kernel (finish)    only for zero iterations: data <- s X0, or
 //                           W <- W - lr s X0.
 // s' = s^2 and s'' = s in the first iteration (the normalization is folded
@@ -22,10 +24,11 @@
 // (zh translation, wiki.whaty.org), sections "Distributed mode" and
 // "SYRK 和融合的 all-reduce".
 //
-// The Gram and A*A are "NT" contractions C[i][j] = sum_k P[i][k] Q[j][k]
-// over K-contiguous rows (of X, of the symmetric A). B X reads rows i of the
-// symmetric B the same way and rows k of X through transposing LDS reads, so
-// X lives in one row-major layout only.
+// All three are "NT" contractions C[i][j] = sum_k P[i][k] Q[j][k] over
+// K-contiguous rows: of X (Gram), of the symmetric A (A*A), of the symmetric
+// B and of X^T (B X). X is kept in both orientations, each written once per
+// iteration, so no product needs transposing LDS reads (on gfx950 those cost
+// a quarter of the loop rate of plain 16-byte fragment reads).
 #include <hip/hip_runtime.h>
 
 #include <utility>
@@ -158,8 +161,13 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
     *reinterpret_cast<OutDesc *>(Vw.blk + Vw.off_scale + kOutDescOffset) = od;
   }
   if (kind == kPrepNs || kind == kPrepStep) {
-    // X0 in wide orientation: this tile's rows as they are, or (tall view)
-    // transposed through the LDS tile
+    // X0 in wide orientation and, when a bf16 B X will read it, X0^T: the
+    // user's tile goes to one of them row by row and to the other transposed
+    // through the LDS tile (wide view: X rows, X^T transposed; tall view:
+    // X^T rows, X transposed)
+    T *XT = Vw.off_xt >= 0 ? reinterpret_cast<T *>(Vw.blk + Vw.off_xt) : nullptr;
+    T *Dd = Vw.tall ? XT : X, *Dt = Vw.tall ? X : XT;
+    const int64_t pd = Vw.tall ? int64_t(Vw.pitch_xt) : px, pt = Vw.tall ? px : int64_t(Vw.pitch_xt);
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
@@ -186,9 +194,9 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
         ss = fmaf(xf, xf, ss);
         tile[row][cc * V + e] = xv.e[e];
       }
-      if (!Vw.tall) *reinterpret_cast<Vec16<T> *>(X + int64_t(gr) * px + gc) = xv;
+      if (Dd) *reinterpret_cast<Vec16<T> *>(Dd + int64_t(gr) * pd + gc) = xv;
     }
-    if (Vw.tall) {
+    if (Dt) {
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < CPT; ++q) {
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
         Vec16<T> tv;
 #pragma unroll
         for (int e = 0; e < V; ++e) tv.e[e] = tile[tcc * V + e][trow];
-        *reinterpret_cast<Vec16<T> *>(X + int64_t(tc * 64 + trow) * px + tr * 64 + tcc * V) = tv;
+        *reinterpret_cast<Vec16<T> *>(Dt + int64_t(tc * 64 + trow) * pt + tr * 64 + tcc * V) = tv;
       }
     }
 #pragma unroll
@@ -461,21 +469,6 @@ __device__ inline void put_trans(char *smem, const EpiCoord &e, int bi, int bj, 
   const int tj = e.jb + bj * 32, ti = e.ib + bi * 32 + r4 * 8;
   *reinterpret_cast<u32x2 *>(smem + tile_off(tj, ti)) = v;
 }
-// Stores the packed accumulators (bits [0, 16)) of a 256 x 256 tile to a
-// row-major matrix from the registers: the same quad transpose as
-// put_direct, then one 8-byte store of 4 consecutive columns per lane.
-__device__ inline void store_direct(bf16 *dst, int64_t pitch, f32x16 (&acc)[4][4], const EpiCoord &e) {
-  for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int p = e.jb & 3;
-      const u32x2 t = quad_transpose(unpack4(a, r4, 0), p);
-      const int ti = e.ib + bi * 32 + r4 * 8 + p, tj = e.jb - p + bj * 32;
-      *reinterpret_cast<u32x2 *>(dst + int64_t(ti) * pitch + tj) = t;
-    }
-  });
-}
-
 template <bool TRANS>
 __device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const EpiCoord &e, int shift) {
   for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
@@ -500,20 +493,6 @@ __device__ inline bf16x8 diag_frag(float v, int lane, int kk) {
 #pragma unroll
   for (int x = 0; x < 8; ++x) f[x] = bf16(x == e ? v : 0.f);
   return f;
-}
-
-// Two ds_read_b64_tr_b16 four rows apart: from a [k][column] LDS stage, lane
-// l receives 8 consecutive k of one column, the B-operand layout of
-// v_mfma_f32_32x32x16_bf16. Within each group of 16 lanes, lane s points at
-// row s >> 2 and columns 4 (s & 3) .. + 3 of a 4 x 16 block; the transposing
-// read hands lane s column s of that block, rows 0..3.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-__device__ inline bf16x8 tr_frag(const char *p) {
-  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
-  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p + 4 * 512));
-  const s16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  return __builtin_bit_cast(bf16x8, z);
 }
 
 template <int PHASE>
@@ -556,9 +535,9 @@ void gemm_bf16_kernel(const GemmArgs args) {
   const int mp = S.mp, np = S.np;
   const int i0 = ti.I * kBM, j0 = ti.J * kBM;
 
-  // P: rows i of the left operand, K-contiguous. Q: rows j, K-contiguous
-  // (Gram, A*A), or rows k of X (B X; B is symmetric, so its rows i serve
-  // as P).
+  // P: rows i of the left operand, Q: rows j of the right one, both
+  // K-contiguous: X (Gram), A (A*A), or B and X^T (B X; B is symmetric, so
+  // its rows i serve as P, and X^T holds the columns of X with k contiguous).
   const bf16 *P, *Q, *P2, *Q2;
   int64_t ld;
   int K;
@@ -573,21 +552,18 @@ void gemm_bf16_kernel(const GemmArgs args) {
     K = args.aa_plain ? mp : 3 * mp;
   } else {
     P = P2 = reinterpret_cast<const bf16 *>(blk + S.off_b);
-    Q = Q2 = reinterpret_cast<const bf16 *>(blk + S.off_xa[args.src]);
+    Q = Q2 = reinterpret_cast<const bf16 *>(blk + S.off_xt[args.src]);
     ld = mp;
     K = mp;
   }
 
-  // Global -> LDS: each wave issues 4 loads per operand per K step.
-  // K-contiguous operand: load q of wave w fills rows (4 w + q) * 16 .. + 15
-  // (64-byte rows, 1 KiB); lane L carries row base + L / 4 and the logical k
-  // chunk that belongs in physical chunk L % 4.
-  // X rows (B X): the stage is 32 rows k x 512 bytes; load q of wave w fills
-  // rows 2 (4 w + q) and + 1; lane L carries physical 16-byte chunk L % 32 of
-  // its row, whose 64-byte unit is the logical unit XOR (k & 3).
+  // Global -> LDS: each wave issues 4 loads per operand per K step. Load q
+  // of wave w fills rows (4 w + q) * 16 .. + 15 of the operand tile (64-byte
+  // rows, 1 KiB); lane L carries row base + L / 4 and the logical k chunk
+  // that belongs in physical chunk L % 4.
   const int lrow0 = lane >> 2;
   const int lphys = lane & 3;
-  int64_t goff[4], qoff[4];
+  int64_t goff[4];
   int loff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -595,20 +571,13 @@ void gemm_bf16_kernel(const GemmArgs args) {
     const int lc = lphys ^ ((row >> 2) & 3);
     goff[q] = int64_t(row) * ld + lc * 8;
     loff[q] = (wv * 4 + q) * 1024;
-    if (PHASE == kBX) {
-      const int kr = (wv * 4 + q) * 2 + (lane >> 5), pc = lane & 31;
-      qoff[q] = int64_t(kr) * np + (((pc >> 2) ^ (kr & 3)) << 5) + (pc & 3) * 8;
-    } else {
-      qoff[q] = goff[q];
-    }
   }
   const int64_t prow0 = int64_t(i0) * ld;
-  const int64_t qrow0 = PHASE == kBX ? int64_t(j0) : int64_t(j0) * ld;
-  const int64_t qkmul = PHASE == kBX ? int64_t(np) : 1;
+  const int64_t qrow0 = int64_t(j0) * ld;
   // B X runs its K loop from the tile's own diagonal block (k = i0) around
   // to i0 - 1: the row tiles that share a column panel then read different
-  // rows of X at any moment instead of the same 32 rows, which spreads the
-  // concurrent X reads over the memory channels. (It also puts the K steps
+  // k of X^T at any moment instead of the same 32, which spreads the
+  // concurrent reads over the memory channels. (It also puts the K steps
   // whose k range equals a block row of the output at iterations
   // 4 wm + bi, the same in every tile.)
   const int krot = PHASE == kBX ? i0 : 0;
@@ -637,15 +606,6 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // multiples of 32 rows)
   const int fa = (wm * 128 + fr) * 64, fb = (wn * 128 + fr) * 64;
   const int fx = (fr >> 2) & 3;
-  // B X: transposing reads of the X stage. Lane s of each 16-lane group
-  // reads row 8 h + (s >> 2) (+ 16 kk + 4 t) at column 4 (s & 3) + 16 g of
-  // block bj; rows k & 3 = 0..3 of one read land in 4 distinct 64-byte units.
-  const int trow = (lane & 15) >> 2;
-  const int qtr = (8 * fh + trow) * 512 + (4 * (lane & 3) + 16 * ((lane >> 4) & 1)) * 2;
-  int qun[4];
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj) qun[bj] = ((4 * wn + bj) ^ trow) << 6;
-
   // issue the loads of K step ks_ into its stage (for A*A, K runs over three
   // segments of length mp: hi*hi, hi*lo, lo*hi)
 #define MUON_GLOAD(ks_)                                                              \
@@ -659,14 +619,13 @@ void gemm_bf16_kernel(const GemmArgs args) {
       pa_ = sgm_ == 2 ? P2 : P;                                                      \
       qa_ = sgm_ == 1 ? Q2 : Q;                                                      \
     }                                                                                \
-    const int64_t qk_ = int64_t(k0_) * qkmul;                                        \
     char *st_ = smem + ((ks_) % kStages) * kStageBytes;                              \
     _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
       __builtin_amdgcn_global_load_lds(                                              \
           (const __attribute__((address_space(1))) void *)(pa_ + prow0 + goff[q] + k0_), \
           (__attribute__((address_space(3))) void *)(st_ + loff[q]), 16, 0, 0);      \
       __builtin_amdgcn_global_load_lds(                                              \
-          (const __attribute__((address_space(1))) void *)(qa_ + qrow0 + qoff[q] + qk_), \
+          (const __attribute__((address_space(1))) void *)(qa_ + qrow0 + goff[q] + k0_), \
           (__attribute__((address_space(3))) void *)(st_ + kOpBytes + loff[q]), 16, 0, 0); \
     }                                                                                \
   } while (0)
@@ -677,13 +636,8 @@ void gemm_bf16_kernel(const GemmArgs args) {
     const int ch_ = (((kk_) * 2 + fh) ^ fx) << 4;                                    \
     _Pragma("unroll") for (int bi = 0; bi < 4; ++bi)                                 \
       af[buf_][bi] = *reinterpret_cast<const bf16x8 *>(As_ + fa + bi * 2048 + ch_);  \
-    if (PHASE == kBX) {                                                              \
-      _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                               \
-        bq[buf_][bj] = tr_frag(Bs_ + (kk_) * 16 * 512 + qtr + qun[bj]);              \
-    } else {                                                                         \
-      _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                               \
-        bq[buf_][bj] = *reinterpret_cast<const bf16x8 *>(Bs_ + fb + bj * 2048 + ch_); \
-    }                                                                                \
+    _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                                 \
+      bq[buf_][bj] = *reinterpret_cast<const bf16x8 *>(Bs_ + fb + bj * 2048 + ch_);   \
   } while (0)
 #define MUON_MFMA(buf_)                                                              \
   do {                                                                               \
@@ -691,28 +645,31 @@ void gemm_bf16_kernel(const GemmArgs args) {
       _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                               \
         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf_][bi], bq[buf_][bj], acc[bi][bj], 0, 0, 0); \
   } while (0)
-  // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
-  // [15:14], expcnt[6:4] and lgkmcnt[11:8] left at their maxima)
-#define MUON_WAIT_VM(n_) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0F70)
-  // One K step. Step ks + 1 landed for this wave (ks + 2, ks + 3 in flight);
-  // after the barrier it has landed for every wave, and every wave has
-  // consumed step ks - 1. A bare s_barrier: the fragment reads still in
-  // flight here target step ks, never the stage the next loads overwrite.
-#define MUON_STEP_CORE(ks_, CAP0_, CAP1_)                                            \
+  // s_waitcnt with vmcnt constrained and lgkmcnt(0) (gfx9 encoding:
+  // vmcnt[3:0] and [15:14], expcnt[6:4] left at its maximum, lgkmcnt[11:8])
+#define MUON_WAIT_VM(n_) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0070)
+  // One K step. Its first half issues the fragment reads of its own k 0..15
+  // beside the MFMAs of the previous step's k 16..31 (their fragments were
+  // read in the previous step), its second half the reads of k 16..31
+  // beside the MFMAs of k 0..15. So step ks reads stage ks only, and the wait
+  // at its top needs only stage ks landed (ks + 1 .. ks + 3 stay in flight):
+  // four steps of latency for each load. lgkmcnt(0) before the barrier: every
+  // fragment read of stage ks - 1 has returned before any wave's loads of
+  // step ks + 4 may overwrite that stage.
+#define MUON_STEP_CORE(ks_, FIRST_, CAP_)                                            \
   do {                                                                               \
-    MUON_WAIT_VM(16);                                                                \
+    MUON_WAIT_VM(24);                                                                \
     __builtin_amdgcn_s_barrier();                                                    \
     MUON_GLOAD((ks_) + 4 < kl ? (ks_) + 4 : kl);                                     \
+    MUON_FRAGS(0, ks_, 0);                                                           \
+    if (!(FIRST_)) MUON_MFMA(1);                                                     \
     MUON_FRAGS(1, ks_, 1);                                                           \
     MUON_MFMA(0);                                                                    \
-    CAP0_;                                                                           \
-    MUON_FRAGS(0, (ks_) + 1, 0); /* stage of ks + 1 (re-reads the last stage at the end) */ \
-    MUON_MFMA(1);                                                                    \
-    CAP1_;                                                                           \
+    CAP_;                                                                            \
   } while (0)
 #define MUON_STEP(ks_)                                                               \
   do {                                                                               \
-    MUON_STEP_CORE(ks_, (void)0, (void)0);                                           \
+    MUON_STEP_CORE(ks_, false, (void)0);                                             \
     __builtin_amdgcn_sched_group_barrier(0x020, 8, 0); /* global->LDS loads first */ \
     _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                 \
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                             \
@@ -724,13 +681,18 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // the 32 output rows of block row bi_, the Q fragments hold exactly the
   // A (or X) values of those outputs, and D Q adds D_mm Q[m][:] to row m.
   // The diagonal goes in as bf16 hi + lo parts (hi only for the small lo
-  // half of A).
+  // half of A). Both k halves are captured at the end of their step.
 #define MUON_CAPTURE(buf_, bi_, dh_, dl_, lo_)                                       \
   do {                                                                               \
     _Pragma("unroll") for (int bj = 0; bj < 4; ++bj) {                               \
       acc[bi_][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dh_[buf_], bq[buf_][bj], acc[bi_][bj], 0, 0, 0); \
       if (lo_) acc[bi_][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dl_[buf_], bq[buf_][bj], acc[bi_][bj], 0, 0, 0); \
     }                                                                                \
+  } while (0)
+#define MUON_CAP2(bi_, dh_, dl_, lo_)                                                \
+  do {                                                                               \
+    MUON_CAPTURE(0, bi_, dh_, dl_, lo_);                                             \
+    MUON_CAPTURE(1, bi_, dh_, dl_, lo_);                                             \
   } while (0)
 
   // Steps past the end re-load the last step into its own stage (the same
@@ -742,12 +704,10 @@ void gemm_bf16_kernel(const GemmArgs args) {
   MUON_GLOAD(1 < kl ? 1 : kl);
   MUON_GLOAD(2 < kl ? 2 : kl);
   MUON_GLOAD(3 < kl ? 3 : kl);
-  MUON_WAIT_VM(24);  // step 0 landed (steps 1..3 in flight; earlier stores done)
-  __builtin_amdgcn_s_barrier();
-  MUON_FRAGS(0, 0, 0);
   int ks = 0;
   if (PHASE == kGram) {
-    for (; ks < nk; ++ks) MUON_STEP(ks);
+    MUON_STEP_CORE(ks, true, (void)0);
+    for (++ks; ks < nk; ++ks) MUON_STEP(ks);
   } else {
     if (PHASE == kAA) {
       // the K step whose k range equals this wave's first output rows
@@ -755,43 +715,54 @@ void gemm_bf16_kernel(const GemmArgs args) {
       const float r = args.r, rh = float(bf16(r));
       const bf16x8 dh[2] = {diag_frag(rh, lane, 0), diag_frag(rh, lane, 1)};
       const bf16x8 dl[2] = {diag_frag(r - rh, lane, 0), diag_frag(r - rh, lane, 1)};
-#define MUON_CAP_STEPS(lo_)                                                          \
+#define MUON_CAP_STEPS(lo_, FIRST_)                                                  \
       do {                                                                           \
-        MUON_STEP_CORE(ks, MUON_CAPTURE(0, 0, dh, dl, lo_), MUON_CAPTURE(1, 0, dh, dl, lo_)); ++ks; \
-        MUON_STEP_CORE(ks, MUON_CAPTURE(0, 1, dh, dl, lo_), MUON_CAPTURE(1, 1, dh, dl, lo_)); ++ks; \
-        MUON_STEP_CORE(ks, MUON_CAPTURE(0, 2, dh, dl, lo_), MUON_CAPTURE(1, 2, dh, dl, lo_)); ++ks; \
-        MUON_STEP_CORE(ks, MUON_CAPTURE(0, 3, dh, dl, lo_), MUON_CAPTURE(1, 3, dh, dl, lo_)); ++ks; \
+        MUON_STEP_CORE(ks, FIRST_, MUON_CAP2(0, dh, dl, lo_)); ++ks;                 \
+        MUON_STEP_CORE(ks, false, MUON_CAP2(1, dh, dl, lo_)); ++ks;                  \
+        MUON_STEP_CORE(ks, false, MUON_CAP2(2, dh, dl, lo_)); ++ks;                  \
+        MUON_STEP_CORE(ks, false, MUON_CAP2(3, dh, dl, lo_)); ++ks;                  \
       } while (0)
       // segment hi*hi: r A_hi (+ its bf16 rounding remainder)
-      for (; ks < c0; ++ks) MUON_STEP(ks);
-      MUON_CAP_STEPS(true);
+      if (c0 == 0) {
+        MUON_CAP_STEPS(true, true);
+      } else {
+        MUON_STEP_CORE(ks, true, (void)0);
+        for (++ks; ks < c0; ++ks) MUON_STEP(ks);
+        MUON_CAP_STEPS(true, false);
+      }
       if (!args.aa_plain) {
         // segment hi*lo: its Q fragments hold A_lo, which is symmetric too
         const int c1 = mp / kBK + c0;
         for (; ks < c1; ++ks) MUON_STEP(ks);
-        MUON_CAP_STEPS(false);
+        MUON_CAP_STEPS(false, false);
       }
 #undef MUON_CAP_STEPS
     } else {
       // K step c0 + bi is loop iteration 4 wm + bi (rotated K loop)
       const int cb = wm * (128 / kBK);
-      for (; ks < cb; ++ks) MUON_STEP(ks);
-#define MUON_CAP_STEP(bi_)                                                           \
+#define MUON_CAP_STEP(bi_, FIRST_)                                                   \
       do {                                                                           \
         const float cv = coef_v[bi_], ch = float(bf16(cv));                          \
         const bf16x8 dh[2] = {diag_frag(ch, lane, 0), diag_frag(ch, lane, 1)};       \
         const bf16x8 dl[2] = {diag_frag(cv - ch, lane, 0), diag_frag(cv - ch, lane, 1)}; \
-        MUON_STEP_CORE(ks, MUON_CAPTURE(0, bi_, dh, dl, true), MUON_CAPTURE(1, bi_, dh, dl, true)); \
+        MUON_STEP_CORE(ks, FIRST_, MUON_CAP2(bi_, dh, dl, true));                    \
         ++ks;                                                                        \
       } while (0)
-      MUON_CAP_STEP(0);
-      MUON_CAP_STEP(1);
-      MUON_CAP_STEP(2);
-      MUON_CAP_STEP(3);
+      if (cb == 0) {
+        MUON_CAP_STEP(0, true);
+      } else {
+        MUON_STEP_CORE(ks, true, (void)0);
+        for (++ks; ks < cb; ++ks) MUON_STEP(ks);
+        MUON_CAP_STEP(0, false);
+      }
+      MUON_CAP_STEP(1, false);
+      MUON_CAP_STEP(2, false);
+      MUON_CAP_STEP(3, false);
 #undef MUON_CAP_STEP
     }
     for (; ks < nk; ++ks) MUON_STEP(ks);
   }
+  MUON_MFMA(1);  // k 16..31 of the last step
   MUON_WAIT_VM(0);  // no load may still target LDS past the K loop
 #undef MUON_GLOAD
 #undef MUON_FRAGS
@@ -800,6 +771,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #undef MUON_STEP_CORE
 #undef MUON_STEP
 #undef MUON_CAPTURE
+#undef MUON_CAP2
 
   // ---------------- epilogues ----------------
   if (PHASE != kBX) __syncthreads();  // every wave is done with the LDS ring
@@ -880,10 +852,11 @@ void gemm_bf16_kernel(const GemmArgs args) {
     }
   } else {
     // X' = s'' ((a + B_ii) X + B_offdiag X), the first term added in the K
-    // loop; stored straight from the registers (no LDS), so the loads of the
-    // next tile of a persistent launch can start right behind the stores
+    // loop; it goes out through LDS twice: X' for the next Gram and X'^T for
+    // the next B X (or, in the last iteration, into the caller's matrix)
     const float sx = args.first ? scale_p[0] : 1.f;
     bf16 *Y = reinterpret_cast<bf16 *>(blk + S.off_xa[args.src ^ 1]);
+    bf16 *Yt = reinterpret_cast<bf16 *>(blk + S.off_xt[args.src ^ 1]);
     for_blocks(acc, [&](f32x16 &a, int, int) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, sx * a[r]));
@@ -898,7 +871,14 @@ void gemm_bf16_kernel(const GemmArgs args) {
       lds_barrier();
       tile_update_user(smem, od, args.lr, od.tall ? j0 : i0, od.tall ? i0 : j0, tid);
     } else {
-      store_direct(Y + int64_t(i0) * np + j0, np, acc, ec);
+      lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
+      fill_tile<false>(smem, acc, ec, 0);
+      lds_barrier();
+      tile_store(smem, Y, np, i0, j0, tid);
+      lds_barrier();
+      fill_tile<true>(smem, acc, ec, 0);
+      lds_barrier();
+      tile_store(smem, Yt, mp, j0, i0, tid);  // X'^T: tile (J, I) of an np x mp matrix
     }
     lds_barrier();  // every wave is done with the LDS ring
   }

@@ -41,6 +41,10 @@ Layout view_layout(int64_t mp, int64_t np, bool bf16, bool distributed) {
     L.xa[p] = off;
     off = align_up(off + mn, 256);
   }
+  for (int p = 0; p < 2; ++p) {
+    L.xt[p] = off;
+    if (bf16) off = align_up(off + mn, 256);
+  }
   L.ahi = off;
   off = align_up(off + mm, 256);
   L.alo = off;
@@ -289,7 +293,7 @@ std::string plan_json(const Plan &p) {
         << ",\"base\":" << sg.base << ",\"stride\":" << sg.stride << ",\"tiles_syrk\":" << sg.tiles_syrk
         << ",\"tiles_gemm\":" << sg.tiles_gemm;
       const Layout L = view_layout(sg.mp, sg.np, p.bf16, p.distributed);
-      o << ",\"layout\":{\"xa\":[" << L.xa[0] << "," << L.xa[1]
+      o << ",\"layout\":{\"xa\":[" << L.xa[0] << "," << L.xa[1] << "],\"xt\":[" << L.xt[0] << "," << L.xt[1]
         << "],\"ahi\":" << L.ahi << ",\"alo\":" << L.alo << ",\"b\":" << L.b << ",\"bdiag\":" << L.bdiag
         << ",\"partials\":" << L.partials << ",\"tri\":" << L.tri
         << ",\"scale\":" << L.scale << ",\"total\":" << L.total << "}}";

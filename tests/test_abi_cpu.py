@@ -263,12 +263,29 @@ def test_plan_distributed_shards():
     assert [c["count"] for c in q["chunks"]] == [4, 4, 4]
 
 
-def test_plan_layout_disjoint():
-    p = mu.muon_plan_info(shapes_descs([(300, 520)]))
-    L = p["chunks"][0]["segments"][0]["layout"]
-    spans = sorted([L["xa"][0], L["xa"][1], L["ahi"], L["alo"], L["b"], L["partials"], L["scale"]])
-    assert spans == sorted(set(spans)) and all(x % 256 == 0 for x in spans)
-    assert L["total"] > L["scale"]
+@pytest.mark.parametrize("dtype", [mu.MUON_BF16, mu.MUON_F32])
+def test_plan_layout_disjoint(dtype):
+    """Every buffer of a view's workspace block is 256-byte aligned, inside the
+    block and disjoint from the others; the bf16 path also holds X^T twice
+    (np x mp, ping-pong), the float32 path no X^T and no lo half of A."""
+    p = mu.muon_plan_info(shapes_descs([(300, 520)], dtype=dtype))
+    seg = p["chunks"][0]["segments"][0]
+    L, mp, np_ = seg["layout"], seg["mp"], seg["np"]
+    es = 2 if dtype == mu.MUON_BF16 else 4
+    bf = dtype == mu.MUON_BF16
+    nparts = (mp // 64) * (np_ // 64)
+    spans = [(L["xa"][0], mp * np_ * es), (L["xa"][1], mp * np_ * es),
+             (L["ahi"], mp * mp * es), (L["b"], mp * mp * es),
+             (L["partials"], nparts * 4), (L["scale"], 16)]
+    if bf:
+        spans += [(L["xt"][0], np_ * mp * es), (L["xt"][1], np_ * mp * es), (L["alo"], mp * mp * es),
+                  (L["bdiag"], mp * 4)]
+    else:
+        assert L["xt"][0] == L["xt"][1] and L["alo"] == L["b"]
+    spans.sort()
+    assert all(off % 256 == 0 for off, _ in spans)
+    assert all(a + n <= b for (a, n), (b, _) in zip(spans, spans[1:]))
+    assert spans[-1][0] + spans[-1][1] <= L["total"]
 
 
 # ---------------------------------------------------------------------------

@@ -159,7 +159,11 @@ def test_bf16_symmetric_intermediates(gpu_lib, split):
         return buf[seg["base"] + off: seg["base"] + off + rows * cols * 2].view(torch.bfloat16).view(rows, cols)
     Ah, Al, B = mat(L["ahi"], mp, mp), mat(L["alo"], mp, mp), mat(L["b"], mp, mp)
     s = 1.0 / (np.linalg.norm(X0) + 1e-7)
-    m = shape[0]
+    m, n = shape
+    # prep wrote X0 and X0^T (the right operand of B X), zero-padded, exactly
+    Xa, Xt = np64(mat(L["xa"][0], mp, np_)), np64(mat(L["xt"][0], np_, mp))
+    assert np.array_equal(Xa[:m, :n], X0) and np.array_equal(Xt, Xa.T)
+    assert not Xa[m:, :].any() and not Xa[:, n:].any()
     Aref = s * s * (X0 @ X0.T)
     if split:
         A = np64(Ah) + np64(Al)

@@ -27,6 +27,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12   # dense bf16 MFMA, 2516.6 TFLOP/s
+# workspace of the timed run: three groups of 384 views for the MoE-layer
+# batch (a 2048 x 7168 view takes 142.6 MB: X and X^T twice, A hi/lo, B)
+WS_GB_DEFAULT = 56.0
 PEAK_HBM_GBS = 8000.0
 
 
@@ -36,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="kimi_moe_layer")
-    p.add_argument("--workspace-gb", type=float, default=32.0)
+    p.add_argument("--workspace-gb", type=float, default=WS_GB_DEFAULT)
     p.add_argument("--pack", choices=["cost", "rr"], default="cost")
     p.add_argument("--aa", choices=["plain", "split"], default="plain",
                    help="A*A from bf16(A) (default) or from A as bf16 hi + lo")
@@ -304,12 +307,13 @@ def main():
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": (recorded_traffic(wl.name, {"gram": "gemm_bf16_kernel<0>", "aa": "gemm_bf16_kernel<1>",
                                                    "bx": "gemm_bf16_kernel<2>"}[dom])
-                        if args.pack == "cost" and args.aa == "plain" and args.workspace_gb == 32.0
+                        if args.pack == "cost" and args.aa == "plain" and args.workspace_gb == WS_GB_DEFAULT
                         else None),
             "flops_per_launch": fl_launch,
             "avg_launch_ms": round(avg_ms, 4),
         }
-        pb = acc.prep_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4)
+        pb = acc.prep_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4,
+                            transposed=wl.dtype == "bf16" and wl.iters > 0)
         out["prep_gbs"] = round(pb / (per_step["prep"][0] * 1e-3) / 1e9, 1) if per_step["prep"][0] > 0 else None
     if args.tp > 0 and phases:
         P = args.tp

@@ -75,8 +75,10 @@ def elementwise_bytes(shapes, elem_size):
     return 6 * n * elem_size
 
 
-def prep_bytes(shapes, elem_size):
+def prep_bytes(shapes, elem_size, transposed=True):
     """HBM bytes of the prep pass: read G and M, write M and the
-    Newton-Schulz source X0 (the update itself runs inside the last B X)."""
+    Newton-Schulz source X0, and X0^T as well when `transposed` (the bf16
+    path with iterations, whose B X reads X with k contiguous). The update
+    itself runs inside the last B X."""
     n = sum(r * c for (r, c) in shapes)
-    return 4 * n * elem_size
+    return (5 if transposed else 4) * n * elem_size

@@ -344,6 +344,33 @@ __device__ inline void tile_store(const char *smem, bf16 *dst, int64_t pitch, in
     *reinterpret_cast<u32x4 *>(dst + int64_t(row0 + row) * pitch + col0 + c * 8) = v;
   }
 }
+// The LDS tile holding a 256 x 256 block in [j][i] order, written to rows i
+// (row0 + i) of a row-major matrix. ds_read_b64_tr_b16 (within each 16-lane
+// group, lane s addresses row s >> 2, columns 4 (s & 3) .. + 3 of a 4 x 16
+// block and receives column s, rows 0..3) reads it transposed: two reads
+// four rows apart hand lane s the 8 consecutive j of row i = 16 ib + s, one
+// 16-byte store. A wave's store covers 16 rows x 64 bytes; its 32 stores the
+// whole width of 64 rows. The 8 (row, chunk) pairs of 32 lanes fall in 16
+// distinct 16-byte slots of the tile swizzle: no bank conflicts.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline s16x4 ds_read_tr(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+}
+__device__ inline void tile_store_tr(const char *smem, bf16 *dst, int64_t pitch, int row0, int col0, int tid) {
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, sl = lane & 15;
+#pragma unroll 8
+  for (int k = 0; k < 32; ++k) {
+    const int u = w * 32 + k, ib = u >> 3, jb = (u & 7) * 32 + g * 8;
+    const int ic = ib * 16 + 4 * (sl & 3), jr = jb + (sl >> 2);
+    const s16x4 x = ds_read_tr(smem + tile_off(jr, ic));
+    const s16x4 y = ds_read_tr(smem + tile_off(jr + 4, ic));
+    const u32x4 v = {uint32_t(uint16_t(x[0])) | (uint32_t(uint16_t(x[1])) << 16),
+                     uint32_t(uint16_t(x[2])) | (uint32_t(uint16_t(x[3])) << 16),
+                     uint32_t(uint16_t(y[0])) | (uint32_t(uint16_t(y[1])) << 16),
+                     uint32_t(uint16_t(y[2])) | (uint32_t(uint16_t(y[3])) << 16)};
+    *reinterpret_cast<u32x4 *>(dst + int64_t(row0 + ib * 16 + sl) * pitch + col0 + jb) = v;
+  }
+}
 // Barrier for LDS hand-offs inside the epilogue: waits for this wave's LDS
 // operations only, not for its global stores (a full __syncthreads() fence
 // would wait for every store of the previous pass to land).
@@ -871,14 +898,13 @@ void gemm_bf16_kernel(const GemmArgs args) {
       lds_barrier();
       tile_update_user(smem, od, args.lr, od.tall ? j0 : i0, od.tall ? i0 : j0, tid);
     } else {
+      // one pass through LDS in [j][i] order: X'^T leaves as its rows, X' as
+      // the transposing reads of the same tile
       lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
-      fill_tile<false>(smem, acc, ec, 0);
-      lds_barrier();
-      tile_store(smem, Y, np, i0, j0, tid);
-      lds_barrier();
       fill_tile<true>(smem, acc, ec, 0);
       lds_barrier();
       tile_store(smem, Yt, mp, j0, i0, tid);  // X'^T: tile (J, I) of an np x mp matrix
+      tile_store_tr(smem, Y, np, i0, j0, tid);
     }
     lds_barrier();  // every wave is done with the LDS ring
   }

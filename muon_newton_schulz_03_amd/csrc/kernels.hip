@@ -699,10 +699,17 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #define MUON_STEP(ks_)                                                               \
   do {                                                                               \
     MUON_STEP_CORE(ks_, false, (void)0);                                             \
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0); /* global->LDS loads first */ \
-    _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                 \
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                             \
+    /* first half: the 8 global->LDS loads, one between each pair of MFMAs, */       \
+    /* with a fragment read after each; second half: one read per 2 MFMAs */         \
+    _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                  \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                             \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
+    }                                                                                \
+    _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                             \
     }                                                                                \
   } while (0)
   // The additive terms of B = b A + c A A and X' = (a + diag B) X + B' X

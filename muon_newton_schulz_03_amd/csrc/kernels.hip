@@ -511,6 +511,19 @@ __device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const EpiCoord
   });
 }
 
+// Block (bi, bj) of the float accumulators, times sc and rounded to bf16
+// on the way, into the LDS tile in [tj][ti] order (8-byte writes): the
+// accumulators are not written back as packed bf16 first.
+__device__ inline void fill_tile_trans_scaled(char *smem, f32x16 (&acc)[4][4], const EpiCoord &e, float sc) {
+  for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const u32x2 v = {pack_bf16(sc * a[r4 * 4 + 1], sc * a[r4 * 4]), pack_bf16(sc * a[r4 * 4 + 3], sc * a[r4 * 4 + 2])};
+      put_trans(smem, e, bi, bj, r4, v);
+    }
+  });
+}
+
 // A-operand fragment of a diagonal matrix v I for one 16-k half (kk) of a
 // 32-k step whose k range equals the 32 output rows of an accumulator block:
 // lane (m = l & 31, h = l >> 5) supplies row m at k = 16 kk + 8 h + e, so
@@ -817,9 +830,10 @@ void gemm_bf16_kernel(const GemmArgs args) {
   float *scale_p = reinterpret_cast<float *>(blk + S.off_scale);
 
   if (PHASE == kGram) {
-    // A = s' X X^T as bf16 hi + lo. Each output tile passes through LDS in
-    // its own row order: A[j][i] (8-byte writes) for the mirror tile (J, I),
-    // A[i][j] for the tile (I, J); a diagonal tile leaves once, symmetrized.
+    // A = s' X X^T as bf16 hi + lo. Each output tile passes through LDS once,
+    // as A[j][i] (8-byte writes): its rows are the mirror tile (J, I), its
+    // transposing reads the tile (I, J); a diagonal tile leaves once,
+    // symmetrized.
     const float sg = args.first ? scale_p[1] : 1.f;
     for_blocks(acc, [&](f32x16 &a, int, int) {
 #pragma unroll
@@ -839,11 +853,8 @@ void gemm_bf16_kernel(const GemmArgs args) {
       if (diag) {
         tile_store_sym(smem, dst, mp, i0, j0, tid);
       } else {
-        tile_store(smem, dst, mp, j0, i0, tid);  // mirror tile (J, I)
-        lds_barrier();
-        fill_tile<false>(smem, acc, ec, shift);
-        lds_barrier();
-        tile_store(smem, dst, mp, i0, j0, tid);  // tile (I, J)
+        tile_store(smem, dst, mp, j0, i0, tid);     // mirror tile (J, I)
+        tile_store_tr(smem, dst, mp, i0, j0, tid);  // tile (I, J)
       }
       lds_barrier();
     }
@@ -881,11 +892,8 @@ void gemm_bf16_kernel(const GemmArgs args) {
     if (diag) {
       tile_store_sym(smem, Bm, mp, i0, j0, tid);
     } else {
-      tile_store(smem, Bm, mp, j0, i0, tid);  // mirror tile (J, I)
-      lds_barrier();
-      fill_tile<false>(smem, acc, ec, 0);
-      lds_barrier();
-      tile_store(smem, Bm, mp, i0, j0, tid);  // tile (I, J)
+      tile_store(smem, Bm, mp, j0, i0, tid);     // mirror tile (J, I)
+      tile_store_tr(smem, Bm, mp, i0, j0, tid);  // tile (I, J)
     }
   } else {
     // X' = s'' ((a + B_ii) X + B_offdiag X), the first term added in the K
@@ -894,11 +902,11 @@ void gemm_bf16_kernel(const GemmArgs args) {
     const float sx = args.first ? scale_p[0] : 1.f;
     bf16 *Y = reinterpret_cast<bf16 *>(blk + S.off_xa[args.src ^ 1]);
     bf16 *Yt = reinterpret_cast<bf16 *>(blk + S.off_xt[args.src ^ 1]);
-    for_blocks(acc, [&](f32x16 &a, int, int) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, sx * a[r]));
-    });
     if (args.last) {
+      for_blocks(acc, [&](f32x16 &a, int, int) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, sx * a[r]));
+      });
       const OutDesc od = *reinterpret_cast<const OutDesc *>(blk + S.off_scale + kOutDescOffset);
       lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
       if (od.tall)
@@ -911,7 +919,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
       // one pass through LDS in [j][i] order: X'^T leaves as its rows, X' as
       // the transposing reads of the same tile
       lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
-      fill_tile<true>(smem, acc, ec, 0);
+      fill_tile_trans_scaled(smem, acc, ec, sx);
       lds_barrier();
       tile_store(smem, Yt, mp, j0, i0, tid);  // X'^T: tile (J, I) of an np x mp matrix
       tile_store_tr(smem, Y, np, i0, j0, tid);

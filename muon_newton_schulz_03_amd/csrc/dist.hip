@@ -17,12 +17,20 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+#include "layout.h"
 
 namespace muon {
 namespace {
 
 
 __device__ inline int64_t tri_row(int64_t i, int64_t mp) { return i * mp - i * (i - 1) / 2; }
+
+// Element offset of A[i][j] in the workspace: k-blocked for bf16, row-major
+// for float32.
+template <typename T>
+__device__ inline int64_t aoff(int64_t i, int64_t j, int64_t mp) {
+  return sizeof(T) == 2 ? kblk(i, j, mp) : i * mp + j;
+}
 
 __device__ inline void locate(const GemmArgs &a, int b, int *seg, int *view, int *row) {
   int s = 0;
@@ -42,11 +50,12 @@ __global__ __launch_bounds__(256) void tri_pack_kernel(const GemmArgs args) {
   char *blk = S.base + int64_t(v) * S.stride;
   const int mp = S.mp;
   float *tri = reinterpret_cast<float *>(blk + S.off_tri) + tri_row(i, mp) - i;
-  const T *hi = reinterpret_cast<const T *>(blk + S.off_ahi) + int64_t(i) * mp;
-  const T *lo = reinterpret_cast<const T *>(blk + S.off_alo) + int64_t(i) * mp;
+  const T *hi = reinterpret_cast<const T *>(blk + S.off_ahi);
+  const T *lo = reinterpret_cast<const T *>(blk + S.off_alo);
   for (int j = i + int(threadIdx.x); j < mp; j += 256) {
-    float x = float(hi[j]);
-    if (sizeof(T) == 2) x += float(lo[j]);
+    const int64_t a = aoff<T>(i, j, mp);
+    float x = float(hi[a]);
+    if (sizeof(T) == 2) x += float(lo[a]);
     tri[j] = x;
   }
 }
@@ -81,8 +90,8 @@ __global__ __launch_bounds__(256) void tri_reduce_kernel(const GemmArgs args) {
       for (int g = 0; g < G; ++g) x += reinterpret_cast<const float *>(blk0 + int64_t(g) * S.stride + S.off_tri)[idx];
       for (int g = 0; g < G; ++g) {
         char *blk = blk0 + int64_t(g) * S.stride;
-        reinterpret_cast<T *>(blk + S.off_ahi)[int64_t(i) * mp + j] = T(x);
-        if (sizeof(T) == 2) reinterpret_cast<T *>(blk + S.off_alo)[int64_t(i) * mp + j] = T(x - float(T(x)));
+        reinterpret_cast<T *>(blk + S.off_ahi)[aoff<T>(i, j, mp)] = T(x);
+        if (sizeof(T) == 2) reinterpret_cast<T *>(blk + S.off_alo)[aoff<T>(i, j, mp)] = T(x - float(T(x)));
       }
     }
     tile[r][c] = x;
@@ -96,8 +105,8 @@ __global__ __launch_bounds__(256) void tri_reduce_kernel(const GemmArgs args) {
     const float x = tile[c][rj];
     for (int g = 0; g < G; ++g) {
       char *blk = blk0 + int64_t(g) * S.stride;
-      reinterpret_cast<T *>(blk + S.off_ahi)[int64_t(j) * mp + i] = T(x);
-      if (sizeof(T) == 2) reinterpret_cast<T *>(blk + S.off_alo)[int64_t(j) * mp + i] = T(x - float(T(x)));
+      reinterpret_cast<T *>(blk + S.off_ahi)[aoff<T>(j, i, mp)] = T(x);
+      if (sizeof(T) == 2) reinterpret_cast<T *>(blk + S.off_alo)[aoff<T>(j, i, mp)] = T(x - float(T(x)));
     }
   }
 }

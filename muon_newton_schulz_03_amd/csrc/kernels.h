@@ -2,10 +2,11 @@
 //
 // Workspace: every view (a whole matrix, or a column block in blockwise mode)
 // owns one block of the caller's workspace holding X (wide orientation,
-// row-major, ping-pong), on the bf16 path also X^T (ping-pong: the right
+// ping-pong), on the bf16 path also X^T (ping-pong: the right
 // operand of B X with k contiguous), the Gram matrix A (bf16 hi/lo halves,
 // or float32), B = b A + c A A, the per-tile partial sums of squares and its
 // scale s = 1/(||X||_F + eps).
+// The float32 path stores them row-major, the bf16 path k-blocked (layout.h).
 // Views of one padded shape sit at a uniform stride ("segment"), so a grouped
 // launch needs only a handful of segment descriptors in its kernel arguments.
 #pragma once
@@ -35,7 +36,7 @@ struct ElemView {
   int64_t ld_g, ld_m, ld_w;  // elements
   char *blk;                 // workspace block of the view
   int64_t off_x;             // X (wide orientation: X^T of the user's view if tall)
-  int64_t off_xt;            // prep: X^T as well (np x mp row-major), or -1
+  int64_t off_xt;            // prep: X^T as well (np x mp), or -1
   int64_t off_part, off_scale;
   int32_t rows, cols;        // view shape, user orientation
   int32_t pitch_x;           // row pitch (elements) of X

@@ -34,6 +34,7 @@
 #include <utility>
 
 #include "kernels.h"
+#include "layout.h"
 
 namespace muon {
 namespace {
@@ -130,6 +131,13 @@ __device__ inline void store_row_chunk(void *base, int64_t ld, int gr, int gc, i
   }
 }
 
+// Element offset of (r, c) in the workspace copy of X or X^T: k-blocked for
+// bf16 (the MFMA operands), row-major for float32.
+template <typename T>
+__device__ inline int64_t xoff(int64_t r, int64_t c, int64_t pitch) {
+  return sizeof(T) == 2 ? kblk(r, c, pitch) : r * pitch + c;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
   constexpr int V = 16 / sizeof(T);      // elements per 16-byte chunk
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
         ss = fmaf(xf, xf, ss);
         tile[row][cc * V + e] = xv.e[e];
       }
-      if (Dd) *reinterpret_cast<Vec16<T> *>(Dd + int64_t(gr) * pd + gc) = xv;
+      if (Dd) *reinterpret_cast<Vec16<T> *>(Dd + xoff<T>(gr, gc, pd)) = xv;
     }
     if (Dt) {
       __syncthreads();
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
         Vec16<T> tv;
 #pragma unroll
         for (int e = 0; e < V; ++e) tv.e[e] = tile[tcc * V + e][trow];
-        *reinterpret_cast<Vec16<T> *>(Dt + int64_t(tc * 64 + trow) * pt + tr * 64 + tcc * V) = tv;
+        *reinterpret_cast<Vec16<T> *>(Dt + xoff<T>(tc * 64 + trow, tr * 64 + tcc * V, pt)) = tv;
       }
     }
 #pragma unroll
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
 #pragma unroll
       for (int q = 0; q < CPT; ++q) {
         const int c = tid + 256 * q, row = c / CPR, cc = c % CPR;
-        const Vec16<T> v = *reinterpret_cast<const Vec16<T> *>(X + int64_t(tc * 64 + row) * px + tr * 64 + cc * V);
+        const Vec16<T> v = *reinterpret_cast<const Vec16<T> *>(X + xoff<T>(tc * 64 + row, tr * 64 + cc * V, px));
 #pragma unroll
         for (int e = 0; e < V; ++e) tile[row][cc * V + e] = v.e[e];
       }
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
 #pragma unroll
         for (int e = 0; e < V; ++e) o[e] = float(tile[cc * V + e][row]) * sf;
       } else {
-        const Vec16<T> ov = *reinterpret_cast<const Vec16<T> *>(X + int64_t(gr) * px + gc);
+        const Vec16<T> ov = *reinterpret_cast<const Vec16<T> *>(X + xoff<T>(gr, gc, px));
 #pragma unroll
         for (int e = 0; e < V; ++e) o[e] = float(ov.e[e]) * sf;
       }
@@ -336,29 +344,36 @@ __device__ inline void for_blocks(f32x16 (&acc)[4][4], F &&f) {
   for_blocks(acc, f, std::make_integer_sequence<int, 16>{});
 }
 
-// tile (256 x 256 at row0, col0 of a row-major matrix with `pitch`) <-> LDS
-__device__ inline void tile_store(const char *smem, bf16 *dst, int64_t pitch, int row0, int col0, int tid) {
+// The LDS tile -> the 256 x 256 tile at (row0, col0) of a k-blocked matrix
+// with `cols` columns: 8 consecutive 16 KiB blocks, written in order (each
+// wave instruction stores 1 KiB: 16 rows x 64 bytes of one block). Within a
+// 16-lane group the 4 rows x 4 chunks read from LDS fall in 16 distinct
+// 16-byte bank slots of the swizzle.
+__device__ inline void tile_store(const char *smem, bf16 *dst, int64_t cols, int row0, int col0, int tid) {
+  bf16 *d = dst + kblk(row0, col0, cols);
 #pragma unroll 8
   for (int k = 0; k < 32; ++k) {
-    const int u = tid + 256 * k, row = u >> 5, c = u & 31;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + row * 512 + (tile_chunk(row, c) << 4));
-    *reinterpret_cast<u32x4 *>(dst + int64_t(row0 + row) * pitch + col0 + c * 8) = v;
+    const int v = tid + 256 * k, kb = v >> 10, row = (v >> 2) & 255, cq = v & 3;
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(smem + row * 512 + (tile_chunk(row, kb * 4 + cq) << 4));
+    *reinterpret_cast<u32x4 *>(d + int64_t(v) * 8) = x;
   }
 }
 // The LDS tile holding a 256 x 256 block in [j][i] order, written to rows i
-// (row0 + i) of a row-major matrix. ds_read_b64_tr_b16 (within each 16-lane
+// (row0 + i) of a k-blocked matrix with `cols` columns. ds_read_b64_tr_b16 (within each 16-lane
 // group, lane s addresses row s >> 2, columns 4 (s & 3) .. + 3 of a 4 x 16
 // block and receives column s, rows 0..3) reads it transposed: two reads
 // four rows apart hand lane s the 8 consecutive j of row i = 16 ib + s, one
 // 16-byte store. A wave's store covers 16 rows x 64 bytes; its 32 stores the
-// whole width of 64 rows. The 8 (row, chunk) pairs of 32 lanes fall in 16
+// whole width of 64 rows; in the k-blocked layout those 16 rows x 64 bytes
+// are 1 KiB of one block. The 8 (row, chunk) pairs of 32 lanes fall in 16
 // distinct 16-byte slots of the tile swizzle: no bank conflicts.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ inline s16x4 ds_read_tr(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
-__device__ inline void tile_store_tr(const char *smem, bf16 *dst, int64_t pitch, int row0, int col0, int tid) {
+__device__ inline void tile_store_tr(const char *smem, bf16 *dst, int64_t cols, int row0, int col0, int tid) {
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, sl = lane & 15;
+  bf16 *d = dst + kblk(row0, col0, cols);
 #pragma unroll 8
   for (int k = 0; k < 32; ++k) {
     const int u = w * 32 + k, ib = u >> 3, jb = (u & 7) * 32 + g * 8;
@@ -369,7 +384,7 @@ __device__ inline void tile_store_tr(const char *smem, bf16 *dst, int64_t pitch,
                      uint32_t(uint16_t(x[2])) | (uint32_t(uint16_t(x[3])) << 16),
                      uint32_t(uint16_t(y[0])) | (uint32_t(uint16_t(y[1])) << 16),
                      uint32_t(uint16_t(y[2])) | (uint32_t(uint16_t(y[3])) << 16)};
-    *reinterpret_cast<u32x4 *>(dst + int64_t(row0 + ib * 16 + sl) * pitch + col0 + jb) = v;
+    *reinterpret_cast<u32x4 *>(d + (jb >> 5) * 8192 + (ib * 16 + sl) * 32 + (jb & 31)) = v;
   }
 }
 // Barrier for LDS hand-offs inside the epilogue: waits for this wave's LDS
@@ -430,8 +445,9 @@ __device__ inline void tile_update_user(const char *smem, const OutDesc &od, flo
 // Diagonal tile: the LDS tile holds L[c][r] = value computed at (r, c).
 // Output row r takes element c from the upper-triangle computation
 // (min(r, c), max(r, c)), so the stored tile is symmetric bit for bit.
-__device__ inline void tile_store_sym(const char *smem, bf16 *dst, int64_t pitch, int row0, int col0, int tid) {
-  bf16 *d = dst + int64_t(row0 + tid) * pitch + col0;
+// Destination: the k-blocked matrix with `cols` columns.
+__device__ inline void tile_store_sym(const char *smem, bf16 *dst, int64_t cols, int row0, int col0, int tid) {
+  bf16 *d = dst + kblk(row0, col0, cols) + tid * 32;
   const int r = tid;
 #pragma unroll 4
   for (int cc = 0; cc < 32; ++cc) {
@@ -441,7 +457,7 @@ __device__ inline void tile_store_sym(const char *smem, bf16 *dst, int64_t pitch
       const int c = 8 * cc + e;
       v[e] = *reinterpret_cast<const bf16 *>(smem + (c >= r ? tile_off(c, r) : tile_off(r, c)));
     }
-    *reinterpret_cast<bf16x8 *>(d + 8 * cc) = v;
+    *reinterpret_cast<bf16x8 *>(d + (cc >> 2) * 8192 + (cc & 3) * 8) = v;
   }
 }
 
@@ -601,16 +617,18 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // Global -> LDS: each wave issues 4 loads per operand per K step. Load q
   // of wave w fills rows (4 w + q) * 16 .. + 15 of the operand tile (64-byte
   // rows, 1 KiB); lane L carries row base + L / 4 and the logical k chunk
-  // that belongs in physical chunk L % 4.
+  // that belongs in physical chunk L % 4. The operands are k-blocked: the
+  // K step at k0 of the 256-row panel at i0 is the 16 KiB block at
+  // i0 * ld + (k0 / 32) * 8192 elements, rows of 32 elements.
   const int lrow0 = lane >> 2;
   const int lphys = lane & 3;
-  int64_t goff[4];
+  int goff[4];
   int loff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = (wv * 4 + q) * 16 + lrow0;
     const int lc = lphys ^ ((row >> 2) & 3);
-    goff[q] = int64_t(row) * ld + lc * 8;
+    goff[q] = row * 32 + lc * 8;
     loff[q] = (wv * 4 + q) * 1024;
   }
   const int64_t prow0 = int64_t(i0) * ld;
@@ -664,10 +682,10 @@ void gemm_bf16_kernel(const GemmArgs args) {
     char *st_ = smem + ((ks_) % kStages) * kStageBytes;                              \
     _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
       __builtin_amdgcn_global_load_lds(                                              \
-          (const __attribute__((address_space(1))) void *)(pa_ + prow0 + goff[q] + k0_), \
+          (const __attribute__((address_space(1))) void *)(pa_ + prow0 + (k0_ >> 5) * 8192 + goff[q]), \
           (__attribute__((address_space(3))) void *)(st_ + loff[q]), 16, 0, 0);      \
       __builtin_amdgcn_global_load_lds(                                              \
-          (const __attribute__((address_space(1))) void *)(qa_ + qrow0 + goff[q] + k0_), \
+          (const __attribute__((address_space(1))) void *)(qa_ + qrow0 + (k0_ >> 5) * 8192 + goff[q]), \
           (__attribute__((address_space(3))) void *)(st_ + kOpBytes + loff[q]), 16, 0, 0); \
     }                                                                                \
   } while (0)
@@ -687,22 +705,22 @@ void gemm_bf16_kernel(const GemmArgs args) {
       _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                               \
         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf_][bi], bq[buf_][bj], acc[bi][bj], 0, 0, 0); \
   } while (0)
-  // s_waitcnt with vmcnt constrained and lgkmcnt(0) (gfx9 encoding:
-  // vmcnt[3:0] and [15:14], expcnt[6:4] left at its maximum, lgkmcnt[11:8])
-#define MUON_WAIT_VM(n_) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0070)
-  // One K step. Its first half issues the fragment reads of its own k 0..15
-  // beside the MFMAs of the previous step's k 16..31 (their fragments were
-  // read in the previous step), its second half the reads of k 16..31
-  // beside the MFMAs of k 0..15. So step ks reads stage ks only, and the wait
-  // at its top needs only stage ks landed (ks + 1 .. ks + 3 stay in flight):
-  // four steps of latency for each load. lgkmcnt(0) before the barrier: every
-  // fragment read of stage ks - 1 has returned before any wave's loads of
-  // step ks + 4 may overwrite that stage.
+  // s_waitcnt with vmcnt constrained (gfx9 encoding: vmcnt[3:0] and [15:14],
+  // expcnt[6:4] and lgkmcnt[11:8] left at their maxima)
+#define MUON_WAIT_VM(n_) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0F70)
+  // One K step reads stage ks only: the fragments of its k 0..15 and of its
+  // k 16..31 (consumed by the MFMAs at the top of the next step). The loads
+  // run three steps ahead: the wait at the top needs stage ks landed (the
+  // 16 loads of ks + 1, ks + 2 stay in flight), and after the barrier the
+  // loads of step ks + 3 go to the stage of step ks - 2, whose fragments
+  // every wave has consumed in the MFMAs of step ks - 1, before reaching this
+  // barrier; so the barrier need not wait for LDS reads. (Four steps ahead
+  // with an LDS wait at the barrier measured 0.4% slower.)
 #define MUON_STEP_CORE(ks_, FIRST_, CAP_)                                            \
   do {                                                                               \
-    MUON_WAIT_VM(24);                                                                \
+    MUON_WAIT_VM(16);                                                                \
     __builtin_amdgcn_s_barrier();                                                    \
-    MUON_GLOAD((ks_) + 4 < kl ? (ks_) + 4 : kl);                                     \
+    MUON_GLOAD((ks_) + 3 < kl ? (ks_) + 3 : kl);                                     \
     MUON_FRAGS(0, ks_, 0);                                                           \
     if (!(FIRST_)) MUON_MFMA(1);                                                     \
     MUON_FRAGS(1, ks_, 1);                                                           \
@@ -712,8 +730,12 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #define MUON_STEP(ks_)                                                               \
   do {                                                                               \
     MUON_STEP_CORE(ks_, false, (void)0);                                             \
-    /* first half: the 8 global->LDS loads, one between each pair of MFMAs, */       \
-    /* with a fragment read after each; second half: one read per 2 MFMAs */         \
+    /* groups (masks: 0x020 global load, 0x100 LDS read, 0x008 MFMA): 8 x */         \
+    /* {load, read, MFMA, read}, then 8 x {MFMA, 2 reads}. What comes out: the */    \
+    /* 8 loads among the first MFMAs, all 16 fragment reads of the step in its */    \
+    /* first half, then the 16 MFMAs of k 0..15 back to back. Spreading the */       \
+    /* reads of k 16..31 over those MFMAs instead (so that each half waits only */   \
+    /* for its own reads) measured 0.3 - 3% slower per GEMM. */                      \
     _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                  \
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                             \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
@@ -752,7 +774,6 @@ void gemm_bf16_kernel(const GemmArgs args) {
   MUON_GLOAD(0);
   MUON_GLOAD(1 < kl ? 1 : kl);
   MUON_GLOAD(2 < kl ? 2 : kl);
-  MUON_GLOAD(3 < kl ? 3 : kl);
   int ks = 0;
   if (PHASE == kGram) {
     MUON_STEP_CORE(ks, true, (void)0);

@@ -30,8 +30,8 @@ constexpr int kGemmTile = 256;
 
 // Byte offsets of the buffers of one view inside its workspace block.
 struct Layout {
-  size_t xa[2];     // X, mp x np row-major (ping-pong)
-  size_t xt[2];     // bf16 path: X^T, np x mp row-major (ping-pong), read by B X
+  size_t xa[2];     // X, mp x np (ping-pong; row-major for float32, k-blocked for bf16)
+  size_t xt[2];     // bf16 path: X^T, np x mp k-blocked (ping-pong), read by B X
   size_t ahi, alo;  // A = X X^T (bf16 hi/lo halves; float32 path uses ahi only)
   size_t b;         // B = b A + c A A (bf16 path: diagonal stored as zero)
   size_t bdiag;     // bf16 path: diagonal of B in float32

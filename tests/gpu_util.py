@@ -39,3 +39,10 @@ def padded(rows, cols, dtype, ld=None, device="cuda", fill=None):
     ld = cols if ld is None else ld
     base = torch.full((rows, ld), float("nan") if fill is None else fill, dtype=dtype, device=device)
     return base, base[:, :cols]
+
+
+def unblock(t, rows, cols):
+    """Row-major copy of a bf16 workspace operand (X, X^T, A or B), which the
+    library keeps k-blocked: blocks of 256 rows x 32 columns, row-major inside,
+    ordered by 256-row panel and then by 32-column block."""
+    return t.reshape(rows // 256, cols // 32, 256, 32).permute(0, 2, 1, 3).reshape(rows, cols).contiguous()

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import np64, padded, relF
+from gpu_util import np64, padded, relF, unblock
 
 pytestmark = pytest.mark.gpu
 
@@ -93,8 +93,8 @@ def test_packed_partial_grams(gpu_lib):
         Xp[:m] = X0[:, p * w:(p + 1) * w]
         part = s * s * (Xp @ Xp.T)
         assert relF(tri.astype(np.float64), part[iu]) < 1e-4
-        Ah = buf[blk + L["ahi"]: blk + L["ahi"] + mp * mp * 2].view(torch.bfloat16).view(mp, mp)
-        Al = buf[blk + L["alo"]: blk + L["alo"] + mp * mp * 2].view(torch.bfloat16).view(mp, mp)
+        Ah = unblock(buf[blk + L["ahi"]: blk + L["ahi"] + mp * mp * 2].view(torch.bfloat16), mp, mp)
+        Al = unblock(buf[blk + L["alo"]: blk + L["alo"] + mp * mp * 2].view(torch.bfloat16), mp, mp)
         As.append((Ah.clone(), Al.clone()))
     for Ah, Al in As:
         assert torch.equal(Ah, As[0][0]) and torch.equal(Al, As[0][1])

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import bf16_round, bf16_ulp_diff, np64, padded, relF
+from gpu_util import bf16_round, bf16_ulp_diff, np64, padded, relF, unblock
 
 pytestmark = pytest.mark.gpu
 
@@ -155,8 +155,8 @@ def test_bf16_symmetric_intermediates(gpu_lib, split):
     mp, np_ = seg["mp"], seg["np"]
     buf = mu._ws.buf
 
-    def mat(off, rows, cols):
-        return buf[seg["base"] + off: seg["base"] + off + rows * cols * 2].view(torch.bfloat16).view(rows, cols)
+    def mat(off, rows, cols):  # the workspace operands are k-blocked
+        return unblock(buf[seg["base"] + off: seg["base"] + off + rows * cols * 2].view(torch.bfloat16), rows, cols)
     Ah, Al, B = mat(L["ahi"], mp, mp), mat(L["alo"], mp, mp), mat(L["b"], mp, mp)
     s = 1.0 / (np.linalg.norm(X0) + 1e-7)
     m, n = shape

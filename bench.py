@@ -164,18 +164,30 @@ def measure_adamw(mu, W, G, steps, warmup):
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
-def recorded_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` recorded in the profile summary for this
-    workload, or None when there is none or the kernel source changed since."""
+def kernel_code_hash():
+    """sha256 of the GEMM kernels' source (kernels.hip and layout.h) with the
+    comments and blank space taken out, so that a comment edit does not void
+    counters taken on the same code."""
     import hashlib
     import re
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "layout.h"):
+        src = open(os.path.join(ROOT, "muon_newton_schulz_03_amd", "csrc", name)).read()
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` recorded in the profile summary for this
+    workload, or None when there is none or the kernel code changed since."""
+    import re
     path = os.path.join(ROOT, "profiles", f"muon_step_{workload}.md")
-    src = os.path.join(ROOT, "muon_newton_schulz_03_amd", "csrc", "kernels.hip")
-    if not os.path.exists(path) or not os.path.exists(src):
+    if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
-    if not m or m.group(1) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    m = re.search(r"^kernel_code_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not m or m.group(1) != kernel_code_hash():
         return None
     m = re.search(r"^traffic_bytes_per_launch " + re.escape(kernel) + r": (\d+)$", text, re.M)
     return int(m.group(1)) if m else None

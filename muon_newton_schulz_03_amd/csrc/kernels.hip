@@ -298,10 +298,11 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const GemmArgs args)
 // Operands stream through a 5-stage LDS ring (stage = 256 rows x 32 k of
 // both operands, 2 x 16 KiB; 160 KiB in all). Global memory goes straight to
 // LDS with global_load_lds_dwordx4 (each lane's 16 bytes land at LDS base +
-// 16 * lane), issued four K steps ahead, so no registers hold staged data and
-// the load latency hides behind four steps of matrix work. One barrier per K
-// step: after it, step ks + 1 is visible to every wave and the stage of step
-// ks - 1 is free for the loads of step ks + 4.
+// 16 * lane), issued three K steps ahead, so no registers hold staged data and
+// the load latency hides behind three steps of matrix work. One barrier per K
+// step: after it, stage ks is visible to every wave and the stage of step
+// ks - 2 is free for the loads of step ks + 3. The operands are k-blocked
+// (layout.h): each K step of an operand tile is one contiguous 16 KiB block.
 //
 // A 64-byte LDS row holds four 16-byte chunks of k, XOR-swizzled by
 // ((row >> 2) & 3): the 16 lanes of a fragment-read group (16 consecutive
@@ -638,8 +639,8 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // panel of X^T then read different k at any moment instead of the same 32
   // (which loads the same lines from 8 CUs at once), yet close enough
   // together that the panel's slabs are still in L2 for the next row tile.
-  // Measured per row-tile offset in K steps: 8 (the tile's own diagonal
-  // block) B X +1.5%, 2 +0.4%, 1 +1.2% against 4.
+  // Measured per row-tile offset in K steps against 4 (k-blocked operands):
+  // 8 (the tile's own diagonal block) +4%; 0, 1 and 2 within 0.5%.
   const int krot = PHASE == kBX ? ti.I * kBxRot * kBK : 0;
 
   // B X: a + diag(B) for the row this lane supplies in each block row

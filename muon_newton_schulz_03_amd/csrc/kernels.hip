@@ -177,22 +177,31 @@ __global__ __launch_bounds__(256) void elem_kernel(const ElemArgs args) {
     T *Dd = Vw.tall ? XT : X, *Dt = Vw.tall ? X : XT;
     const int64_t pd = Vw.tall ? int64_t(Vw.pitch_xt) : px, pt = Vw.tall ? px : int64_t(Vw.pitch_xt);
     float ss = 0.f;
+    // every chunk's loads first (the M stores below may alias them as far as
+    // the compiler knows, so it would not move a later chunk's loads above
+    // them): CPT chunks of G and of M in flight per thread
+    float g[CPT][V], m[CPT][V];
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + 256 * q, row = c / CPR, cc = c % CPR;
+      const int gr = tr * 64 + row, gc = tc * 64 + cc * V;
+      if (kind == kPrepStep) load_row_chunk<T>(Vw.g, Vw.ld_g, gr, gc, Vw.rows, Vw.cols, Vw.vec & 1, g[q]);
+      load_row_chunk<T>(Vw.m, Vw.ld_m, gr, gc, Vw.rows, Vw.cols, Vw.vec & 2, m[q]);
+    }
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int c = tid + 256 * q, row = c / CPR, cc = c % CPR;
       const int gr = tr * 64 + row, gc = tc * 64 + cc * V;
       float x[V];
       if (kind == kPrepStep) {
-        float g[V], m[V];
-        load_row_chunk<T>(Vw.g, Vw.ld_g, gr, gc, Vw.rows, Vw.cols, Vw.vec & 1, g);
-        load_row_chunk<T>(Vw.m, Vw.ld_m, gr, gc, Vw.rows, Vw.cols, Vw.vec & 2, m);
 #pragma unroll
-        for (int e = 0; e < V; ++e) m[e] = fmaf(args.beta, m[e], g[e]);
-        store_row_chunk<T>(Vw.m, Vw.ld_m, gr, gc, Vw.rows, Vw.cols, Vw.vec & 2, m);
+        for (int e = 0; e < V; ++e) m[q][e] = fmaf(args.beta, m[q][e], g[q][e]);
+        store_row_chunk<T>(Vw.m, Vw.ld_m, gr, gc, Vw.rows, Vw.cols, Vw.vec & 2, m[q]);
 #pragma unroll
-        for (int e = 0; e < V; ++e) x[e] = args.nesterov ? fmaf(args.beta, m[e], g[e]) : m[e];
+        for (int e = 0; e < V; ++e) x[e] = args.nesterov ? fmaf(args.beta, m[q][e], g[q][e]) : m[q][e];
       } else {
-        load_row_chunk<T>(Vw.m, Vw.ld_m, gr, gc, Vw.rows, Vw.cols, Vw.vec & 2, x);
+#pragma unroll
+        for (int e = 0; e < V; ++e) x[e] = m[q][e];
       }
       Vec16<T> xv;
 #pragma unroll

@@ -726,20 +726,30 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // every wave has consumed in the MFMAs of step ks - 1, before reaching this
   // barrier; so the barrier need not wait for LDS reads. (Four steps ahead
   // with an LDS wait at the barrier measured 0.4% slower.)
-#define MUON_STEP_CORE(ks_, FIRST_, CAP_)                                            \
+  // TAIL_: the step may be one of the last three, which issue no loads (all
+  // K steps are in flight already), so fewer loads may stay outstanding at
+  // its top: 8 when one step remains to land after this one, 0 at the last.
+#define MUON_STEP_BODY(ks_, FIRST_, CAP_, TAIL_)                                     \
   do {                                                                               \
-    MUON_WAIT_VM(16);                                                                \
+    if (!(TAIL_) || (ks_) + 2 <= kl)                                                 \
+      MUON_WAIT_VM(16);                                                              \
+    else if ((ks_) + 1 == kl)                                                        \
+      MUON_WAIT_VM(8);                                                               \
+    else                                                                             \
+      MUON_WAIT_VM(0);                                                               \
     __builtin_amdgcn_s_barrier();                                                    \
-    MUON_GLOAD((ks_) + 3 < kl ? (ks_) + 3 : kl);                                     \
+    if (!(TAIL_) || (ks_) + 3 <= kl) MUON_GLOAD((ks_) + 3);                          \
     MUON_FRAGS(0, ks_, 0);                                                           \
     if (!(FIRST_)) MUON_MFMA(1);                                                     \
     MUON_FRAGS(1, ks_, 1);                                                           \
     MUON_MFMA(0);                                                                    \
     CAP_;                                                                            \
   } while (0)
+#define MUON_STEP_CORE(ks_, FIRST_, CAP_) MUON_STEP_BODY(ks_, FIRST_, CAP_, true)
+  // a step with ks + 3 <= kl (no tail checks), with its schedule
 #define MUON_STEP(ks_)                                                               \
   do {                                                                               \
-    MUON_STEP_CORE(ks_, false, (void)0);                                             \
+    MUON_STEP_BODY(ks_, false, (void)0, false);                                      \
     /* groups (masks: 0x020 global load, 0x100 LDS read, 0x008 MFMA): 8 x */         \
     /* {load, read, MFMA, read}, then 8 x {MFMA, 2 reads}. What comes out: the */    \
     /* 8 loads among the first MFMAs, all 16 fragment reads of the step in its */    \
@@ -776,18 +786,19 @@ void gemm_bf16_kernel(const GemmArgs args) {
     MUON_CAPTURE(1, bi_, dh_, dl_, lo_);                                             \
   } while (0)
 
-  // Steps past the end re-load the last step into its own stage (the same
-  // bytes again); this keeps 8 loads per wave per step, so the vmcnt
-  // arithmetic below is the same in every iteration.
+  // Every K step is loaded once; K >= 256, so nk >= 8. MUON_STEP runs the
+  // steps with ks + 3 <= kl, MUON_STEP_CORE the first, the capture and the
+  // last three.
   const int kl = nk - 1;
   bf16x8 af[2][4], bq[2][4];
   MUON_GLOAD(0);
-  MUON_GLOAD(1 < kl ? 1 : kl);
-  MUON_GLOAD(2 < kl ? 2 : kl);
+  MUON_GLOAD(1);
+  MUON_GLOAD(2);
   int ks = 0;
   if (PHASE == kGram) {
     MUON_STEP_CORE(ks, true, (void)0);
-    for (++ks; ks < nk; ++ks) MUON_STEP(ks);
+    for (++ks; ks + 3 <= kl; ++ks) MUON_STEP(ks);
+    for (; ks < nk; ++ks) MUON_STEP_CORE(ks, false, (void)0);
   } else {
     if (PHASE == kAA) {
       // the K step whose k range equals this wave's first output rows
@@ -841,7 +852,8 @@ void gemm_bf16_kernel(const GemmArgs args) {
       MUON_CAP_STEP(3, false);
 #undef MUON_CAP_STEP
     }
-    for (; ks < nk; ++ks) MUON_STEP(ks);
+    for (; ks + 3 <= kl; ++ks) MUON_STEP(ks);
+    for (; ks < nk; ++ks) MUON_STEP_CORE(ks, false, (void)0);
   }
   MUON_MFMA(1);  // k 16..31 of the last step
   MUON_WAIT_VM(0);  // no load may still target LDS past the K loop
@@ -850,6 +862,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #undef MUON_MFMA
 #undef MUON_WAIT_VM
 #undef MUON_STEP_CORE
+#undef MUON_STEP_BODY
 #undef MUON_STEP
 #undef MUON_CAPTURE
 #undef MUON_CAP2

@@ -4,6 +4,8 @@
 
 A step is one full Muon step (momentum, Newton-Schulz with five iterations,
 weight update) over every matrix of the workload, inputs resident in HBM.
+Defaults: 3 untimed warm-up steps, 10 timed steps; `step_ms` gives the
+median, p90, min and max of the per-step times from HIP events.
 Default workload: the Kimi-K2-MoE-layer-shaped batch, 384 experts x
 (2048x7168 gate, 2048x7168 up, 7168x2048 down) = 1152 bf16 matrices.
 
@@ -18,7 +20,9 @@ on a bounded sample of the same matrices.
 """
 import argparse
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -36,8 +40,8 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=5)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="kimi_moe_layer")
     p.add_argument("--workspace-gb", type=float, default=WS_GB_DEFAULT)
     p.add_argument("--pack", choices=["cost", "rr"], default="cost")
@@ -248,12 +252,18 @@ def main():
     if timing:
         mu.muon_set_phase_timing(True)
         mu.muon_phase_times()  # clear
+    # per-step HIP events on the launch stream (the library launches on the
+    # current stream), besides the wall clock around the whole timed region
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for k in range(args.steps):
         step()
+        ev[k + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    per_step = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps))
     phases = mu.muon_phase_times() if timing else None
     mu.muon_set_phase_timing(False)
     ms_step = elapsed * 1e3 / args.steps
@@ -290,6 +300,9 @@ def main():
             "workspace_gib": round(ws_bytes / 2**30, 2),
             "groups": len(plan["chunks"]),
         },
+        "step_ms": {"median": round(statistics.median(per_step), 3),
+                    "p90": round(per_step[math.ceil(0.9 * len(per_step)) - 1], 3),
+                    "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
         "tflops_nominal": round(tflops_nom, 2),
         "pct_peak_alg": round(100 * tflops_alg / PEAK_BF16_TFLOPS, 2),
         "pct_peak_nominal": round(100 * tflops_nom / PEAK_BF16_TFLOPS, 2),

@@ -244,7 +244,11 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       ga.src = it & 1;
       ga.first = it == 0 ? 1 : 0;
       set_tiles(true);
+      // Gram: persistent workgroups, one per CU, each looping over tiles of
+      // its XCD's range (measured -0.8% against one workgroup per tile)
+      ga.persistent = (slots > 0 && ga.total_tiles > slots) ? slots : 0;
       e = timed(kTGram, st, [&] { return launch_gemm(ga, kGram, bf16, st); });
+      ga.persistent = 0;
       if (e != hipSuccess) return hip_fail(e, "gram launch");
       if (plan.distributed) {
         // the all-reduce of the partial Grams, simulated on this GPU: one
@@ -268,7 +272,10 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
         if (e != hipSuccess) return hip_fail(e, "triangle reduce launch");
         set_tiles(true);
       }
+      // A*A (short K loop as well): persistent workgroups (measured -1.5%)
+      ga.persistent = (slots > 0 && ga.total_tiles > slots) ? slots : 0;
       e = timed(kTAA, st, [&] { return launch_gemm(ga, kAA, bf16, st); });
+      ga.persistent = 0;
       if (e != hipSuccess) return hip_fail(e, "A*A launch");
       set_tiles(false);
       // B X (short K loop): persistent workgroups, so that a tile's epilogue

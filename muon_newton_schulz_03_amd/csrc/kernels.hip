@@ -939,6 +939,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
       tile_store(smem, Bm, mp, j0, i0, tid);     // mirror tile (J, I)
       tile_store_tr(smem, Bm, mp, i0, j0, tid);  // tile (I, J)
     }
+    lds_barrier();  // in a persistent launch the next tile's loads reuse the LDS
   } else {
     // X' = s'' ((a + B_ii) X + B_offdiag X), the first term added in the K
     // loop; it goes out through LDS twice: X' for the next Gram and X'^T for

@@ -118,6 +118,31 @@ def test_bf16_step_batch(gpu_lib, nesterov):
         assert bf16_ulp_diff(np64(W[i]), expect).max() <= 1
 
 
+@pytest.mark.parametrize("iters,coeffs", [(1, None), (2, None), (7, None), (3, (2.0, -1.5, 0.5))])
+def test_bf16_step_iters_and_coeffs(gpu_lib, iters, coeffs):
+    """muon_step with other iteration counts (iters = 1: the first B X, which
+    applies the normalization, is also the one that writes the weights) and
+    user coefficients, against the oracle with the same (float32-rounded)
+    coefficients."""
+    import muon_newton_schulz_03_amd as mu
+    c = mu.DEFAULT_COEFFS if coeffs is None else coeffs
+    c32 = tuple(float(np.float32(x)) for x in c)
+    shapes = [(300, 520), (520, 300), (256, 768)]
+    G = [rand(s, torch.bfloat16, 400 + i, std=1e-3)[1] for i, s in enumerate(shapes)]
+    M = [rand(s, torch.bfloat16, 500 + i, std=1e-2)[1] for i, s in enumerate(shapes)]
+    G0, M0 = [np64(t) for t in G], [np64(t) for t in M]
+    beta = float(np.float32(0.95))
+    Wz = [torch.zeros_like(t) for t in G]
+    gpu_lib.muon_step(Wz, G, M, lr=-1.0, beta=beta, iters=iters, coeffs=c)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        O_ref, _, _ = oracle.muon_step(np.zeros(shapes[i]), G0[i], M0[i], lr=-1.0, beta=beta,
+                                       iters=iters, coeffs=c32)
+        err = relF(np64(Wz[i]), O_ref)
+        print(f"{shapes[i]} iters {iters} coeffs {c} O relF {err:.3e}")
+        assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("shape,k", [((512, 1536), 3), ((1024, 768), 4), ((300, 520), 2)])
 def test_bf16_blockwise(gpu_lib, shape, k):
     import muon_newton_schulz_03_amd as mu

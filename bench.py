@@ -340,6 +340,7 @@ def main():
         pb = acc.prep_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4,
                             transposed=wl.dtype == "bf16" and wl.iters > 0)
         out["prep_gbs"] = round(pb / (per_step["prep"][0] * 1e-3) / 1e9, 1) if per_step["prep"][0] > 0 else None
+        out["prep_frac_hbm"] = round(out["prep_gbs"] / PEAK_HBM_GBS, 4) if out["prep_gbs"] else None
     if args.tp > 0 and phases:
         P = args.tp
         red = per_step.get("reduce", (0.0, 0))[0]

@@ -1,5 +1,6 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (muon_step, cost packing, a 32 GiB workspace).
+benchmark times (muon_step, cost packing, A*A from bf16(A), the benchmark's
+56 GiB workspace: the Kimi-K2 MoE-layer batch runs in 3 groups of 384).
 
 Whole-step checks on sampled matrices against the float64 oracle:
 * the orthogonalized update O (run with W = 0 and lr = -1, so W_new = O
@@ -24,7 +25,7 @@ from gpu_util import bf16_round, bf16_ulp_diff, np64, relF
 
 pytestmark = pytest.mark.gpu
 
-WS_CAP = 32 << 30
+WS_CAP = 56 << 30  # the benchmark's default workspace
 LR32 = float(np.float32(0.02))
 BETA32 = float(np.float32(0.95))
 

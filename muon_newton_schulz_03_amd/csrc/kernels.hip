@@ -27,8 +27,10 @@
 // All three are "NT" contractions C[i][j] = sum_k P[i][k] Q[j][k] over
 // K-contiguous rows: of X (Gram), of the symmetric A (A*A), of the symmetric
 // B and of X^T (B X). X is kept in both orientations, each written once per
-// iteration, so no product needs transposing LDS reads (on gfx950 those cost
-// a quarter of the loop rate of plain 16-byte fragment reads).
+// iteration, so no product needs transposing LDS reads (in a probe of the K
+// loop on gfx950 they took it from 68% to 51% of the clock-scaled peak). The
+// bf16 operands are stored k-blocked (layout.h), so each K step of an operand
+// tile is one contiguous 16 KiB block.
 #include <hip/hip_runtime.h>
 
 #include <utility>

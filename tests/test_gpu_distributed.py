@@ -40,6 +40,24 @@ def test_distributed_bf16_matches_whole_matrix(gpu_lib, shape, shards):
     assert err <= BF16_TOL
 
 
+def test_distributed_full_size(gpu_lib):
+    """The tensor-parallel benchmark's shape: two 2048 x 7168 MoE matrices,
+    each in 8 column shards of 2048 x 896 (a persistent Gram, the packed
+    exchange of 8 partials and B X per shard), against the float64 oracle of
+    the whole matrix."""
+    import muon_newton_schulz_03_amd as mu
+    xs = [rand((2048, 7168), torch.bfloat16, 70 + i) for i in range(2)]
+    refs = [oracle.newton_schulz(np64(x)) for x in xs]
+    ys = [x.clone() for x in xs]
+    gpu_lib.muon_ns_batched(ys, iters=5, mode=mu.MUON_NS_DISTRIBUTED | mu.MUON_PACK_COST,
+                            col_blocks=[8, 8])
+    torch.cuda.synchronize()
+    for y, ref in zip(ys, refs):
+        err = relF(np64(y), ref)
+        print(f"2048x7168 x8 shards: relF {err:.3e}")
+        assert err <= BF16_TOL
+
+
 def test_distributed_f32(gpu_lib):
     import muon_newton_schulz_03_amd as mu
     X = rand((64, 384), torch.float32, 5, std=1.0)

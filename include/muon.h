@@ -46,7 +46,8 @@ typedef enum muon_status {
   MUON_ERR_DTYPE = 3,       /* unknown dtype or a mix of dtypes             */
   MUON_ERR_ALIGN = 4,       /* data not aligned to its element size, or a
                                workspace not aligned to 256 bytes           */
-  MUON_ERR_ALIAS = 5,       /* written matrices overlap other matrices      */
+  MUON_ERR_ALIAS = 5,       /* written matrices overlap other matrices, or
+                               a matrix reaches into the workspace           */
   MUON_ERR_WORKSPACE = 6,   /* no workspace, or smaller than required       */
   MUON_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed   */
 } muon_status;
@@ -58,9 +59,11 @@ typedef enum muon_dtype { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  * boundaries (16-byte aligned data and ld * sizeof(dtype) a multiple of 16)
  * take the vectorized load/store path; any other pitch takes a slower
  * element-by-element path.
- * col_blocks is used only with MUON_NS_BLOCKWISE: the columns are split into
- * col_blocks equal blocks (col_blocks must divide cols); 0 or 1 means the
- * whole matrix. */
+ * col_blocks is read only under MUON_NS_BLOCKWISE and MUON_NS_DISTRIBUTED
+ * and ignored otherwise. Blockwise: the columns are split into col_blocks
+ * equal blocks, each orthogonalized on its own. Distributed: col_blocks is
+ * the number of column shards P (the same for every matrix of the call). In
+ * both, col_blocks must divide cols; 0 or 1 means the whole matrix. */
 typedef struct muon_mat {
   void *data;
   int64_t rows;
@@ -173,7 +176,9 @@ muon_status muon_workspace_min_size(const muon_mat *descs, int32_t n_mats, uint3
 /* Caller-owned device workspace for this thread's subsequent calls.
  * device_ptr must be 256-byte aligned; (NULL, 0) clears it. The contents
  * need no initialization. Two calls in flight on different streams must use
- * different workspaces. */
+ * different workspaces. No matrix of a call may reach into
+ * [device_ptr, device_ptr + bytes) (first to last byte of each matrix):
+ * such a call returns MUON_ERR_ALIAS. */
 muon_status muon_set_workspace(void *device_ptr, size_t bytes);
 
 /* Options used by muon_step (and eps by muon_ns_batched) on this thread.

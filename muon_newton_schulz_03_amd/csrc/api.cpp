@@ -323,8 +323,11 @@ muon_status muon_ns_batched(const muon_mat *descs, int32_t n_mats, int32_t iters
   const muon_mat *arrays[1] = {descs};
   const bool writable[1] = {true};
   if (!check_alias(arrays, writable, 1, n_mats, &err)) return fail(err);
+  const char *names[1] = {"descs"};
   Plan plan;
-  if (!need_workspace(&err) || !build_plan(descs, n_mats, iters, mode, g_state.ws_bytes, &plan, &err))
+  if (!need_workspace(&err) ||
+      !check_workspace_alias(arrays, names, 1, n_mats, g_state.ws, g_state.ws_bytes, &err) ||
+      !build_plan(descs, n_mats, iters, mode, g_state.ws_bytes, &plan, &err))
     return fail(err);
   Sources src;
   src.data = descs;
@@ -345,8 +348,11 @@ muon_status muon_step(const muon_mat *params, const muon_mat *grads, const muon_
   const muon_mat *arrays[3] = {params, grads, moms};
   const bool writable[3] = {true, false, true};
   if (!check_alias(arrays, writable, 3, n_mats, &err)) return fail(err);
+  const char *names[3] = {"params", "grads", "moms"};
   Plan plan;
-  if (!need_workspace(&err) || !build_plan(params, n_mats, g_state.iters, mode, g_state.ws_bytes, &plan, &err))
+  if (!need_workspace(&err) ||
+      !check_workspace_alias(arrays, names, 3, n_mats, g_state.ws, g_state.ws_bytes, &err) ||
+      !build_plan(params, n_mats, g_state.iters, mode, g_state.ws_bytes, &plan, &err))
     return fail(err);
   Sources src;
   src.W = params;

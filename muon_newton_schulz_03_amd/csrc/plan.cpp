@@ -139,6 +139,20 @@ bool matrices_overlap(const muon_mat &a, const muon_mat &b) {
   return false;
 }
 
+bool check_workspace_alias(const muon_mat *const *arrays, const char *const *names, int narrays, int32_t n,
+                           const void *ws, size_t ws_bytes, Error *err) {
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(ws), w1 = w0 + ws_bytes;
+  for (int a = 0; a < narrays; ++a)
+    for (int32_t i = 0; i < n; ++i) {
+      const muon_mat &x = arrays[a][i];
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(x.data);
+      const uintptr_t hi = lo + (size_t(x.rows - 1) * x.ld + x.cols) * dtype_size(x.dtype);
+      if (lo < w1 && w0 < hi)
+        return err->set(MUON_ERR_ALIAS, std::string(names[a]) + fmt("[%lld] overlaps the workspace", i));
+    }
+  return true;
+}
+
 bool check_alias(const muon_mat *const *arrays, const bool *writable, int narrays, int32_t n, Error *err) {
   struct Item { uintptr_t lo, hi; int arr; int32_t idx; };
   std::vector<Item> items;

@@ -103,6 +103,10 @@ bool validate_step_triplets(const muon_mat *w, const muon_mat *g, const muon_mat
 // flags which of the arrays are written.
 bool check_alias(const muon_mat *const *arrays, const bool *writable, int narrays, int32_t n,
                  Error *err);
+// No matrix of the call may reach into the workspace [ws, ws + ws_bytes)
+// (extent test: the first to the last byte of each matrix).
+bool check_workspace_alias(const muon_mat *const *arrays, const char *const *names, int narrays, int32_t n,
+                           const void *ws, size_t ws_bytes, Error *err);
 bool validate_mode(uint32_t mode, Error *err);
 
 // Orders the views, groups them into chunks that fit `ws_bytes` (0 = as

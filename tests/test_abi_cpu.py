@@ -110,6 +110,28 @@ def test_adamw_validation_codes(lib):
     assert call(W, G, [desc(4, 8, dtype=f32, ptr=FAKE + 16)], V) == mu.MUON_ERR_ALIAS
 
 
+def test_workspace_overlap_rejected(lib):
+    """A matrix that reaches into the workspace is rejected before anything is
+    enqueued (the workspace is fake and never dereferenced: every call here
+    fails validation)."""
+    ws = FAKE * 8
+    try:
+        mu.muon_set_workspace(ws, 1 << 20)
+        inside = desc(4, 8, ptr=ws + 4096)
+        assert lib.muon_ns_batched(mu.mats([inside]), 1, 5, None, 0) == mu.MUON_ERR_ALIAS
+        assert "workspace" in mu.muon_last_error()
+        straddle = desc(64, 64, ptr=ws - 256)  # starts before, ends inside
+        assert lib.muon_ns_batched(mu.mats([straddle]), 1, 5, None, 0) == mu.MUON_ERR_ALIAS
+        W, G, M = desc(4, 8, ptr=FAKE), desc(4, 8, ptr=FAKE * 2), desc(4, 8, ptr=ws + (1 << 20) - 16)
+        assert lib.muon_step(mu.mats([W]), mu.mats([G]), mu.mats([M]), 1, 0.02, 0.95, 0) == mu.MUON_ERR_ALIAS
+        assert "moms[0]" in mu.muon_last_error()
+        G = desc(4, 8, ptr=ws + 1024)  # read-only buffers may not sit there either
+        M = desc(4, 8, ptr=FAKE * 3)
+        assert lib.muon_step(mu.mats([W]), mu.mats([G]), mu.mats([M]), 1, 0.02, 0.95, 0) == mu.MUON_ERR_ALIAS
+    finally:
+        mu.muon_set_workspace(None, 0)
+
+
 def test_alias_exact_for_interleaved_views(lib):
     # two column blocks of one 8 x 64 bf16 buffer do not overlap element-wise
     left = desc(8, 32, ld=64)
@@ -152,7 +174,7 @@ def test_options_and_workspace_args(lib):
 def test_workspace_too_small_is_rejected(lib):
     d = [desc(300, 520)]
     need = mu.muon_workspace_min_size(d)
-    assert lib.muon_set_workspace(ctypes.c_void_p(FAKE), need - 256) == mu.MUON_OK
+    assert lib.muon_set_workspace(ctypes.c_void_p(FAKE * 8), need - 256) == mu.MUON_OK
     try:
         assert lib.muon_ns_batched(mu.mats(d), 1, 5, None, 0) == mu.MUON_ERR_WORKSPACE
     finally:

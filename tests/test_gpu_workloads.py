@@ -9,12 +9,13 @@ Whole-step checks on sampled matrices against the float64 oracle:
 * the weight update (real W, lr = 0.02) within 1 bf16 ulp of
   rn_bf16(W - lr O), O taken from the first run (the path is deterministic).
 
-For the 7168 x 18432 matrices a float64 oracle run of all five iterations
-takes minutes on the host, so there the check is a property that holds at any
-size: one Newton-Schulz iteration, recomputed exactly in float64 for sampled
-rows from the device's own stored input of that iteration. It is applied to
-the first iteration (from the normalized momentum) and to the fifth (from the
-device's fourth iterate).
+The 7168 x 18432 (wide) and 18432 x 7168 (tall) Kimi-K2 dense matrices get
+the same whole-step checks, one matrix per test (a float64 oracle step on one
+of them is ~23 TFLOP of host BLAS work, tens of seconds on the host cores).
+Beside them, a property that holds at any size: one Newton-Schulz iteration,
+recomputed exactly in float64 for sampled rows from the device's own stored
+input of that iteration, applied to the first iteration (from the normalized
+momentum) and to the fifth (from the device's fourth iterate).
 """
 import numpy as np
 import pytest
@@ -30,11 +31,11 @@ LR32 = float(np.float32(0.02))
 BETA32 = float(np.float32(0.95))
 
 
-def run_step_checks(gpu_lib, name, sample, aa_mode=None):
+def run_step_checks(gpu_lib, name, sample, aa_mode=None, shapes=None, seed=None):
     import muon_newton_schulz_03_amd as mu
     from muon_newton_schulz_03_amd.workloads import WORKLOADS, make_inputs
     wl = WORKLOADS[name]
-    W, G, M = make_inputs(wl)
+    W, G, M = make_inputs(wl, shapes=shapes, seed=seed)
     torch.cuda.synchronize()
     aa = mu.MUON_AA_PLAIN if aa_mode is None else aa_mode
     print(f"{name}: {len(W)} matrices, sample {sample}, A*A mode {aa:#x}", flush=True)
@@ -83,6 +84,17 @@ def test_kimi_moe_layer_full(gpu_lib):
 
 def test_kimi_dense_blockwise_full(gpu_lib):
     run_step_checks(gpu_lib, "kimi_dense_blockwise", [0])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("index", [0, 2])
+def test_kimi_dense_step_full(gpu_lib, index):
+    """Whole muon_step on one Kimi-K2 dense matrix: 7168 x 18432 (index 0,
+    wide) or 18432 x 7168 (index 2, tall: transposed in and out, and its
+    weight update written through the tall path of the fused epilogue)."""
+    from muon_newton_schulz_03_amd.workloads import WORKLOADS
+    wl = WORKLOADS["kimi_dense"]
+    run_step_checks(gpu_lib, "kimi_dense", [0], shapes=wl.shapes[index:index + 1], seed=wl.seed + index)
 
 
 @pytest.mark.parametrize("name", ["qwen3_block", "kimi_moe_layer", "kimi_dense_blockwise"])

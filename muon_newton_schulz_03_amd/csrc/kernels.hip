@@ -303,17 +303,20 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const GemmArgs args)
 }
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core kernel: 256x256 output tile, 4 waves (2x2), each wave
-// 128x128 = 4x4 blocks of v_mfma_f32_32x32x16_bf16.
+// bf16 matrix-core kernel: 256x256 output tile, 8 waves (two per SIMD), wave
+// w covering rows 128 (w mod 2) and columns 64 (w / 2) as 4x2 blocks of
+// v_mfma_f32_32x32x16_bf16 (128 accumulators: two waves per SIMD leave each
+// wave 256 registers).
 //
 // Operands stream through a 5-stage LDS ring (stage = 256 rows x 32 k of
 // both operands, 2 x 16 KiB; 160 KiB in all). Global memory goes straight to
-// LDS with global_load_lds_dwordx4 (each lane's 16 bytes land at LDS base +
-// 16 * lane), issued three K steps ahead, so no registers hold staged data and
-// the load latency hides behind three steps of matrix work. One barrier per K
-// step: after it, stage ks is visible to every wave and the stage of step
-// ks - 2 is free for the loads of step ks + 3. The operands are k-blocked
-// (layout.h): each K step of an operand tile is one contiguous 16 KiB block.
+// LDS with buffer_load_dwordx4 ... lds (each lane's 16 bytes land at LDS base
+// + 16 * lane), issued by waves 0..3 only, three K steps ahead, so no
+// registers hold staged data and the load latency hides behind three steps
+// of matrix work. One barrier per K step: after it, stage ks is visible to
+// every wave and the stage of step ks - 2 is free for the loads of step
+// ks + 3. The operands are k-blocked (layout.h): each K step of an operand
+// tile is one contiguous 16 KiB block.
 //
 // A 64-byte LDS row holds four 16-byte chunks of k, XOR-swizzled by
 // ((row >> 2) & 3): the 16 lanes of a fragment-read group (16 consecutive
@@ -329,6 +332,10 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const GemmArgs args)
 constexpr int kBM = 256, kBK = 32, kStages = 5;
 constexpr int kOpBytes = kBM * kBK * 2;          // one operand tile, one stage (16 KiB)
 constexpr int kStageBytes = 2 * kOpBytes;        // both operands
+constexpr int kWaves = 8;                        // two per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 2;                           // 32-column accumulator blocks per wave (wave tile 128 x 64)
+constexpr int kLoaders = 4;                      // waves 0..3, one per SIMD, issue every operand load
 constexpr int kBxRot = 4;                         // B X: K-loop offset per row tile, in K steps
 
 // ---------------------------------------------------------------------------
@@ -345,15 +352,15 @@ __device__ inline int tile_off(int row, int col) {
   return row * 512 + (tile_chunk(row, col >> 3) << 4) + (col & 7) * 2;
 }
 
-// Calls f(acc[bi][bj], bi, bj) for the 16 accumulator blocks with
-// compile-time indices, so the accumulators stay in registers.
+// Calls f(acc[bi][bj], bi, bj) for the 4 x kBN accumulator blocks of a wave
+// with compile-time indices, so the accumulators stay in registers.
 template <class F, int... N>
-__device__ inline void for_blocks(f32x16 (&acc)[4][4], F &&f, std::integer_sequence<int, N...>) {
-  (f(acc[N / 4][N % 4], N / 4, N % 4), ...);
+__device__ inline void for_blocks(f32x16 (&acc)[4][kBN], F &&f, std::integer_sequence<int, N...>) {
+  (f(acc[N / kBN][N % kBN], N / kBN, N % kBN), ...);
 }
 template <class F>
-__device__ inline void for_blocks(f32x16 (&acc)[4][4], F &&f) {
-  for_blocks(acc, f, std::make_integer_sequence<int, 16>{});
+__device__ inline void for_blocks(f32x16 (&acc)[4][kBN], F &&f) {
+  for_blocks(acc, f, std::make_integer_sequence<int, 4 * kBN>{});
 }
 
 // The LDS tile -> the 256 x 256 tile at (row0, col0) of a k-blocked matrix
@@ -364,8 +371,8 @@ __device__ inline void for_blocks(f32x16 (&acc)[4][4], F &&f) {
 __device__ inline void tile_store(const char *smem, bf16 *dst, int64_t cols, int row0, int col0, int tid) {
   bf16 *d = dst + kblk(row0, col0, cols);
 #pragma unroll 8
-  for (int k = 0; k < 32; ++k) {
-    const int v = tid + 256 * k, kb = v >> 10, row = (v >> 2) & 255, cq = v & 3;
+  for (int k = 0; k < 8192 / kThreads; ++k) {
+    const int v = tid + kThreads * k, kb = v >> 10, row = (v >> 2) & 255, cq = v & 3;
     const u32x4 x = *reinterpret_cast<const u32x4 *>(smem + row * 512 + (tile_chunk(row, kb * 4 + cq) << 4));
     *reinterpret_cast<u32x4 *>(d + int64_t(v) * 8) = x;
   }
@@ -378,7 +385,8 @@ __device__ inline void tile_store(const char *smem, bf16 *dst, int64_t cols, int
 // 16-byte store. A wave's store covers 16 rows x 64 bytes; its 32 stores the
 // whole width of 64 rows; in the k-blocked layout those 16 rows x 64 bytes
 // are 1 KiB of one block. The 8 (row, chunk) pairs of 32 lanes fall in 16
-// distinct 16-byte slots of the tile swizzle: no bank conflicts.
+// distinct 16-byte slots of the tile swizzle: no bank conflicts. The 8 waves
+// take 16 of the 128 (16-row, 32-column) pieces each.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ inline s16x4 ds_read_tr(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
@@ -387,8 +395,8 @@ __device__ inline void tile_store_tr(const char *smem, bf16 *dst, int64_t cols, 
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, sl = lane & 15;
   bf16 *d = dst + kblk(row0, col0, cols);
 #pragma unroll 8
-  for (int k = 0; k < 32; ++k) {
-    const int u = w * 32 + k, ib = u >> 3, jb = (u & 7) * 32 + g * 8;
+  for (int k = 0; k < 128 / kWaves; ++k) {
+    const int u = w * (128 / kWaves) + k, ib = u >> 3, jb = (u & 7) * 32 + g * 8;
     const int ic = ib * 16 + 4 * (sl & 3), jr = jb + (sl >> 2);
     const s16x4 x = ds_read_tr(smem + tile_off(jr, ic));
     const s16x4 y = ds_read_tr(smem + tile_off(jr + 4, ic));
@@ -416,18 +424,18 @@ __device__ inline void lds_barrier() {
 __device__ inline void tile_update_user(const char *smem, const OutDesc &od, float lr, int row0, int col0, int tid) {
   const bool vec16 = reinterpret_cast<uintptr_t>(od.out) % 16 == 0 && (od.ld * 2) % 16 == 0;
   // 16 runs per pass, their W loads all issued before the first is used
-  for (int k0 = 0; k0 < 32; k0 += 16) {
+  for (int k0 = 0; k0 < 8192 / kThreads; k0 += 16) {
     u32x4 w[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int u = tid + 256 * (k0 + k), ur = row0 + (u >> 5), uc = col0 + (u & 31) * 8;
+      const int u = tid + kThreads * (k0 + k), ur = row0 + (u >> 5), uc = col0 + (u & 31) * 8;
       w[k] = u32x4{0u, 0u, 0u, 0u};
       if (od.update && vec16 && ur < od.rows && uc + 8 <= od.cols)
         w[k] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(od.out) + int64_t(ur) * od.ld + uc);
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int u = tid + 256 * (k0 + k), row = u >> 5, c = u & 31;
+      const int u = tid + kThreads * (k0 + k), row = u >> 5, c = u & 31;
       const int ur = row0 + row, uc = col0 + c * 8;
       if (ur >= od.rows || uc >= od.cols) continue;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + row * 512 + (tile_chunk(row, c) << 4));
@@ -457,12 +465,13 @@ __device__ inline void tile_update_user(const char *smem, const OutDesc &od, flo
 // Diagonal tile: the LDS tile holds L[c][r] = value computed at (r, c).
 // Output row r takes element c from the upper-triangle computation
 // (min(r, c), max(r, c)), so the stored tile is symmetric bit for bit.
-// Destination: the k-blocked matrix with `cols` columns.
+// Destination: the k-blocked matrix with `cols` columns. Thread t writes
+// row t mod 256, the half t / 256 of its 32 16-byte runs.
 __device__ inline void tile_store_sym(const char *smem, bf16 *dst, int64_t cols, int row0, int col0, int tid) {
-  bf16 *d = dst + kblk(row0, col0, cols) + tid * 32;
-  const int r = tid;
+  const int r = tid & 255, c0 = (tid >> 8) * (32 * 256 / kThreads);
+  bf16 *d = dst + kblk(row0, col0, cols) + r * 32;
 #pragma unroll 4
-  for (int cc = 0; cc < 32; ++cc) {
+  for (int cc = c0; cc < c0 + 32 * 256 / kThreads; ++cc) {
     bf16x8 v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -474,9 +483,9 @@ __device__ inline void tile_store_sym(const char *smem, bf16 *dst, int64_t cols,
 }
 
 // Accumulator element (r4 * 4 + q) of block (bi, bj) sits at tile row
-// ti = wm*128 + bi*32 + r4*8 + fh*4 + q and tile column tj = wn*128 + bj*32 + fr.
+// ti = wm*128 + bi*32 + r4*8 + fh*4 + q and tile column tj = wn*64 + bj*32 + fr.
 struct EpiCoord {
-  int ib, jb;  // wm*128 + fh*4, wn*128 + fr
+  int ib, jb;  // wm*128 + fh*4, wn*64 + fr
 };
 
 // Accumulators converted once and kept bit-packed in place: the bf16 bit
@@ -498,7 +507,7 @@ __device__ inline u32x2 unpack4(const f32x16 &a, int r4, int shift) {
 // writes block (bi, bj) of the packed accumulators into the LDS tile,
 // transposed ([tj][ti], 8-byte writes) or direct ([ti][tj], 2-byte writes)
 template <bool TRANS>
-__device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const struct EpiCoord &e, int shift);
+__device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][kBN], const struct EpiCoord &e, int shift);
 
 // [ti][tj] orientation. Within each quad of lanes (4 consecutive columns)
 // the 4 x 4 block of bf16 (4 rows x 4 columns) is transposed with two DPP
@@ -526,7 +535,7 @@ __device__ inline void put_trans(char *smem, const EpiCoord &e, int bi, int bj, 
   *reinterpret_cast<u32x2 *>(smem + tile_off(tj, ti)) = v;
 }
 template <bool TRANS>
-__device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const EpiCoord &e, int shift) {
+__device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][kBN], const EpiCoord &e, int shift) {
   for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -539,14 +548,14 @@ __device__ inline void fill_tile(char *smem, f32x16 (&acc)[4][4], const EpiCoord
   });
 }
 
-// Block (bi, bj) of the float accumulators, times sc and rounded to bf16
-// on the way, into the LDS tile in [tj][ti] order (8-byte writes): the
-// accumulators are not written back as packed bf16 first.
-__device__ inline void fill_tile_trans_scaled(char *smem, f32x16 (&acc)[4][4], const EpiCoord &e, float sc) {
+// Block (bi, bj) of the float accumulators, rounded to bf16 on the way,
+// into the LDS tile in [tj][ti] order (8-byte writes): the accumulators are
+// not written back as packed bf16 first.
+__device__ inline void fill_tile_trans_f32(char *smem, f32x16 (&acc)[4][kBN], const EpiCoord &e) {
   for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const u32x2 v = {pack_bf16(sc * a[r4 * 4 + 1], sc * a[r4 * 4]), pack_bf16(sc * a[r4 * 4 + 3], sc * a[r4 * 4 + 2])};
+      const u32x2 v = {pack_bf16(a[r4 * 4 + 1], a[r4 * 4]), pack_bf16(a[r4 * 4 + 3], a[r4 * 4 + 2])};
       put_trans(smem, e, bi, bj, r4, v);
     }
   });
@@ -564,15 +573,39 @@ __device__ inline bf16x8 diag_frag(float v, int lane, int kk) {
   return f;
 }
 
-template <int PHASE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Buffer resource over the 4 GiB from p (raw, untyped loads; the third
+// dword is the gfx9 default format), and a 16-byte-per-lane load from it
+// straight into LDS (lane L's bytes land at lds + 16 L).
+__device__ inline __amdgpu_buffer_rsrc_t panel_rsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, -1, 0x00020000);
+}
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
+// Eight waves, two per SIMD (waves w and w + 4), each 128 x 64 outputs
+// (4 x 2 blocks of v_mfma_f32_32x32x16_bf16). Only waves 0..3, one per SIMD,
+// issue the operand loads: a wave that waits to issue a load stalls its own
+// instruction stream, and the SIMD's other wave keeps the matrix core busy
+// meanwhile. Loop probe (256 CUs, L2-resident operands, cycles per 32-k step
+// against 1024 of matrix work): four waves of 128 x 128, every wave loading,
+// 61.5%; eight waves all loading 75%; eight waves with four loading 82.8%;
+// eight waves with no loads at all 86.8%. The buffer form of the LDS load
+// (scalar base, 32-bit lane offset, the K step in the scalar offset) needs no
+// per-load address arithmetic: 75% against 68% with 64-bit lane addresses.
+// LAST (B X only): the last iteration, which writes the caller's matrices
+// instead of X' and X'^T (a separate instantiation: one epilogue per kernel
+// keeps the register allocation within the 256 registers of a wave).
+template <int PHASE, bool LAST = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(const GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
 
   // the wave index goes through readfirstlane so that the compiler sees it
   // (and the K-loop bounds derived from it) as uniform
   const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv & 1, wn = wv >> 1;
+  const bool loader = wv < kLoaders;
 
   // Tiles of this workgroup: one (the grid covers every tile), or, in a
   // persistent launch (8 S workgroups, S per XCD), the tiles begin + slot,
@@ -626,25 +659,26 @@ void gemm_bf16_kernel(const GemmArgs args) {
     K = mp;
   }
 
-  // Global -> LDS: each wave issues 4 loads per operand per K step. Load q
-  // of wave w fills rows (4 w + q) * 16 .. + 15 of the operand tile (64-byte
-  // rows, 1 KiB); lane L carries row base + L / 4 and the logical k chunk
-  // that belongs in physical chunk L % 4. The operands are k-blocked: the
-  // K step at k0 of the 256-row panel at i0 is the 16 KiB block at
-  // i0 * ld + (k0 / 32) * 8192 elements, rows of 32 elements.
+  // Global -> LDS: each loader wave issues 4 loads per operand per K step.
+  // Load q of wave w fills rows (4 w + q) * 16 .. + 15 of the operand tile
+  // (64-byte rows, 1 KiB); lane L carries row base + L / 4 and the logical k
+  // chunk that belongs in physical chunk L % 4. The operands are k-blocked:
+  // the K step at k0 of the 256-row panel at i0 is the 16 KiB block at
+  // i0 * ld + (k0 / 32) * 8192 elements, rows of 32 elements; the buffer
+  // resource points at the panel, the K step goes in the scalar offset.
   const int lrow0 = lane >> 2;
   const int lphys = lane & 3;
-  int goff[4];
+  uint32_t gob[4];
   int loff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = (wv * 4 + q) * 16 + lrow0;
     const int lc = lphys ^ ((row >> 2) & 3);
-    goff[q] = row * 32 + lc * 8;
+    gob[q] = uint32_t(row * 32 + lc * 8) * 2u;
     loff[q] = (wv * 4 + q) * 1024;
   }
-  const int64_t prow0 = int64_t(i0) * ld;
-  const int64_t qrow0 = int64_t(j0) * ld;
+  const __amdgpu_buffer_rsrc_t rP = panel_rsrc(P + int64_t(i0) * ld), rQ = panel_rsrc(Q + int64_t(j0) * ld);
+  const __amdgpu_buffer_rsrc_t rP2 = panel_rsrc(P2 + int64_t(i0) * ld), rQ2 = panel_rsrc(Q2 + int64_t(j0) * ld);
   // B X starts its K loop kBxRot K steps further on in each row tile
   // (k = kBxRot * 32 I) and wraps around: the row tiles that share a column
   // panel of X^T then read different k at any moment instead of the same 32
@@ -663,11 +697,11 @@ void gemm_bf16_kernel(const GemmArgs args) {
     for (int bi = 0; bi < 4; ++bi) coef_v[bi] = args.a + bdiag[bi * 32];
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kBN];
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int bj = 0; bj < kBN; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
@@ -676,29 +710,28 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // byte offset of this lane's fragment rows inside an operand tile; the
   // swizzle term (row >> 2) & 3 depends on the lane only (block bases are
   // multiples of 32 rows)
-  const int fa = (wm * 128 + fr) * 64, fb = (wn * 128 + fr) * 64;
+  const int fa = (wm * 128 + fr) * 64, fb = (wn * 64 + fr) * 64;
   const int fx = (fr >> 2) & 3;
   // issue the loads of K step ks_ into its stage (for A*A, K runs over three
   // segments of length mp: hi*hi, hi*lo, lo*hi)
 #define MUON_GLOAD(ks_)                                                              \
   do {                                                                               \
-    int k0_ = (ks_) * kBK;                                                           \
-    if (PHASE == kBX) k0_ = k0_ + krot < K ? k0_ + krot : k0_ + krot - K;            \
-    const bf16 *pa_ = P, *qa_ = Q;                                                   \
-    if (PHASE == kAA) {                                                              \
-      const int sgm_ = k0_ / mp;                                                     \
-      k0_ -= sgm_ * mp;                                                              \
-      pa_ = sgm_ == 2 ? P2 : P;                                                      \
-      qa_ = sgm_ == 1 ? Q2 : Q;                                                      \
-    }                                                                                \
-    char *st_ = smem + ((ks_) % kStages) * kStageBytes;                              \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
-      __builtin_amdgcn_global_load_lds(                                              \
-          (const __attribute__((address_space(1))) void *)(pa_ + prow0 + (k0_ >> 5) * 8192 + goff[q]), \
-          (__attribute__((address_space(3))) void *)(st_ + loff[q]), 16, 0, 0);      \
-      __builtin_amdgcn_global_load_lds(                                              \
-          (const __attribute__((address_space(1))) void *)(qa_ + qrow0 + (k0_ >> 5) * 8192 + goff[q]), \
-          (__attribute__((address_space(3))) void *)(st_ + kOpBytes + loff[q]), 16, 0, 0); \
+    if (loader) {                                                                    \
+      int k0_ = (ks_) * kBK;                                                         \
+      if (PHASE == kBX) k0_ = k0_ + krot < K ? k0_ + krot : k0_ + krot - K;          \
+      __amdgpu_buffer_rsrc_t ra_ = rP, rb_ = rQ;                                     \
+      if (PHASE == kAA) {                                                            \
+        const int sgm_ = k0_ / mp;                                                   \
+        k0_ -= sgm_ * mp;                                                            \
+        ra_ = sgm_ == 2 ? rP2 : rP;                                                  \
+        rb_ = sgm_ == 1 ? rQ2 : rQ;                                                  \
+      }                                                                              \
+      char *st_ = smem + ((ks_) % kStages) * kStageBytes;                            \
+      const uint32_t so_ = uint32_t(k0_ >> 5) * 16384u;                              \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
+        load_lds16(ra_, st_ + loff[q], gob[q], so_);                                 \
+        load_lds16(rb_, st_ + kOpBytes + loff[q], gob[q], so_);                      \
+      }                                                                              \
     }                                                                                \
   } while (0)
 #define MUON_FRAGS(buf_, ks_, kk_)                                                   \
@@ -708,18 +741,23 @@ void gemm_bf16_kernel(const GemmArgs args) {
     const int ch_ = (((kk_) * 2 + fh) ^ fx) << 4;                                    \
     _Pragma("unroll") for (int bi = 0; bi < 4; ++bi)                                 \
       af[buf_][bi] = *reinterpret_cast<const bf16x8 *>(As_ + fa + bi * 2048 + ch_);  \
-    _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                                 \
+    _Pragma("unroll") for (int bj = 0; bj < kBN; ++bj)                               \
       bq[buf_][bj] = *reinterpret_cast<const bf16x8 *>(Bs_ + fb + bj * 2048 + ch_);   \
   } while (0)
 #define MUON_MFMA(buf_)                                                              \
   do {                                                                               \
     _Pragma("unroll") for (int bi = 0; bi < 4; ++bi)                                 \
-      _Pragma("unroll") for (int bj = 0; bj < 4; ++bj)                               \
+      _Pragma("unroll") for (int bj = 0; bj < kBN; ++bj)                             \
         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf_][bi], bq[buf_][bj], acc[bi][bj], 0, 0, 0); \
   } while (0)
   // s_waitcnt with vmcnt constrained (gfx9 encoding: vmcnt[3:0] and [15:14],
-  // expcnt[6:4] and lgkmcnt[11:8] left at their maxima)
-#define MUON_WAIT_VM(n_) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0F70)
+  // expcnt[6:4] and lgkmcnt[11:8] left at their maxima), in the loader waves
+  // only: the others have no load in flight that targets LDS, and the
+  // barrier after the loaders' wait publishes their stages to every wave
+#define MUON_WAIT_VM(n_)                                                             \
+  do {                                                                               \
+    if (loader) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0F70); \
+  } while (0)
   // One K step reads stage ks only: the fragments of its k 0..15 and of its
   // k 16..31 (consumed by the MFMAs at the top of the next step). The loads
   // run three steps ahead: the wait at the top needs stage ks landed (the
@@ -748,27 +786,8 @@ void gemm_bf16_kernel(const GemmArgs args) {
     CAP_;                                                                            \
   } while (0)
 #define MUON_STEP_CORE(ks_, FIRST_, CAP_) MUON_STEP_BODY(ks_, FIRST_, CAP_, true)
-  // a step with ks + 3 <= kl (no tail checks), with its schedule
-#define MUON_STEP(ks_)                                                               \
-  do {                                                                               \
-    MUON_STEP_BODY(ks_, false, (void)0, false);                                      \
-    /* groups (masks: 0x020 global load, 0x100 LDS read, 0x008 MFMA): 8 x */         \
-    /* {load, read, MFMA, read}, then 8 x {MFMA, 2 reads}. What comes out: the */    \
-    /* 8 loads among the first MFMAs, all 16 fragment reads of the step in its */    \
-    /* first half, then the 16 MFMAs of k 0..15 back to back. Spreading the */       \
-    /* reads of k 16..31 over those MFMAs instead (so that each half waits only */   \
-    /* for its own reads) measured 0.3 - 3% slower per GEMM. */                      \
-    _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                  \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                             \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
-    }                                                                                \
-    _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                  \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                             \
-    }                                                                                \
-  } while (0)
+  // a step with ks + 3 <= kl (no tail checks), in the compiler's order
+#define MUON_STEP(ks_) MUON_STEP_BODY(ks_, false, (void)0, false)
   // The additive terms of B = b A + c A A and X' = (a + diag B) X + B' X
   // enter as products with a diagonal matrix: in the K step whose 32 k are
   // the 32 output rows of block row bi_, the Q fragments hold exactly the
@@ -777,7 +796,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // half of A). Both k halves are captured at the end of their step.
 #define MUON_CAPTURE(buf_, bi_, dh_, dl_, lo_)                                       \
   do {                                                                               \
-    _Pragma("unroll") for (int bj = 0; bj < 4; ++bj) {                               \
+    _Pragma("unroll") for (int bj = 0; bj < kBN; ++bj) {                             \
       acc[bi_][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dh_[buf_], bq[buf_][bj], acc[bi_][bj], 0, 0, 0); \
       if (lo_) acc[bi_][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dl_[buf_], bq[buf_][bj], acc[bi_][bj], 0, 0, 0); \
     }                                                                                \
@@ -792,7 +811,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // steps with ks + 3 <= kl, MUON_STEP_CORE the first, the capture and the
   // last three.
   const int kl = nk - 1;
-  bf16x8 af[2][4], bq[2][4];
+  bf16x8 af[2][4], bq[2][kBN];
   MUON_GLOAD(0);
   MUON_GLOAD(1);
   MUON_GLOAD(2);
@@ -871,7 +890,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
 
   // ---------------- epilogues ----------------
   if (PHASE != kBX) __syncthreads();  // every wave is done with the LDS ring
-  const EpiCoord ec{wm * 128 + fh * 4, wn * 128 + fr};
+  const EpiCoord ec{wm * 128 + fh * 4, wn * 64 + fr};
   const bool diag = (PHASE != kBX) && ti.I == ti.J;
   float *scale_p = reinterpret_cast<float *>(blk + S.off_scale);
 
@@ -910,17 +929,19 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] *= args.c;
     });
-    // The diagonal of B stays in float32 (bdiag); B stores it as zero. Only
-    // blocks (bb, bb) of the waves with wm == wn in a diagonal tile hold
-    // diagonal elements: row 8 r4 + 4 fh + q equals column fr for the lanes
-    // with fh == (fr >> 2) & 1, in register (fr >> 3) * 4 + (fr & 3).
+    // The diagonal of B stays in float32 (bdiag); B stores it as zero. In a
+    // diagonal tile, block (bi, bj) of wave (wm, wn) covers rows
+    // 128 wm + 32 bi and columns 64 wn + 32 bj, so the waves with
+    // wn / 2 == wm hold diagonal elements, in their blocks with
+    // bi == 2 (wn mod 2) + bj: row 8 r4 + 4 fh + q equals column fr for the
+    // lanes with fh == (fr >> 2) & 1, in register (fr >> 3) * 4 + (fr & 3).
     float *bdiag = reinterpret_cast<float *>(blk + S.off_bdiag);
     bf16 *Bm = reinterpret_cast<bf16 *>(blk + S.off_b);
-    if (diag && wm == wn) {
+    if (diag && (wn >> 1) == wm) {
       const bool holder = fh == ((fr >> 2) & 1);
       const int rr = (fr >> 3) * 4 + (fr & 3);
       for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
-        if (bi != bj) return;
+        if (bi != 2 * (wn & 1) + bj) return;
         float x = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) x = r == rr ? a[r] : x;
@@ -949,10 +970,16 @@ void gemm_bf16_kernel(const GemmArgs args) {
     const float sx = args.first ? scale_p[0] : 1.f;
     bf16 *Y = reinterpret_cast<bf16 *>(blk + S.off_xa[args.src ^ 1]);
     bf16 *Yt = reinterpret_cast<bf16 *>(blk + S.off_xt[args.src ^ 1]);
-    if (args.last) {
+    // scaled in place, ahead of the branch, so that the scaled values never
+    // live beside the unscaled ones (with 256 registers per wave that spills)
+    for_blocks(acc, [&](f32x16 &a, int, int) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[r] *= sx;
+    });
+    if (LAST) {
       for_blocks(acc, [&](f32x16 &a, int, int) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, sx * a[r]));
+        for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, a[r]));
       });
       const OutDesc od = *reinterpret_cast<const OutDesc *>(blk + S.off_scale + kOutDescOffset);
       lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
@@ -966,7 +993,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
       // one pass through LDS in [j][i] order: X'^T leaves as its rows, X' as
       // the transposing reads of the same tile
       lds_barrier();  // every wave is done with the LDS ring (its last fragment reads)
-      fill_tile_trans_scaled(smem, acc, ec, sx);
+      fill_tile_trans_f32(smem, acc, ec);
       lds_barrier();
       tile_store(smem, Yt, mp, j0, i0, tid);  // X'^T: tile (J, I) of an np x mp matrix
       tile_store_tr(smem, Y, np, i0, j0, tid);
@@ -1108,12 +1135,17 @@ hipError_t launch_norm_finalize(const GemmArgs &a, int views, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs &a, int phase, bool bf16, hipStream_t s) {
   if (a.total_tiles <= 0) return hipSuccess;
-  const dim3 grid(a.persistent ? a.persistent : a.total_tiles), block(256);
+  const dim3 grid(a.persistent ? a.persistent : a.total_tiles), block(bf16 ? kThreads : 256);
   if (bf16) {
     switch (phase) {
       case kGram: hipLaunchKernelGGL(gemm_bf16_kernel<kGram>, grid, block, 0, s, a); break;
       case kAA: hipLaunchKernelGGL(gemm_bf16_kernel<kAA>, grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL(gemm_bf16_kernel<kBX>, grid, block, 0, s, a); break;
+      default:
+        if (a.last)
+          hipLaunchKernelGGL((gemm_bf16_kernel<kBX, true>), grid, block, 0, s, a);
+        else
+          hipLaunchKernelGGL(gemm_bf16_kernel<kBX>, grid, block, 0, s, a);
+        break;
     }
   } else {
     switch (phase) {

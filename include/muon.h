@@ -84,7 +84,10 @@ typedef struct muon_mat {
                                     order given (round robin)                */
 #define MUON_PACK_COST 0x010u    /* ... in descending cost order             */
 #define MUON_AA_PLAIN 0x000u     /* A*A and b A from bf16-rounded A
-                                    (1 product)                              */
+                                    (1 product); honoured up to 12
+                                    iterations, above that the split form
+                                    runs (the plain form's error nears the
+                                    bf16 path's 2e-2 bound at ~20)          */
 #define MUON_AA_SPLIT 0x100u     /* A*A and b A from A as bf16 hi + lo halves
                                     (3 products: hi hi + hi lo + lo hi);
                                     about 1.3x less error, 3x the A*A work   */

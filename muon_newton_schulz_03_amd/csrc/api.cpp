@@ -123,7 +123,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
     ga.c = coeffs[2];
     ga.r = coeffs[1] / coeffs[2];
     ga.eps = eps;
-    ga.aa_plain = (plan.mode & MUON_AA_SPLIT) ? 0 : 1;
+    ga.aa_plain = ((plan.mode & MUON_AA_SPLIT) || iters > kPlainMaxIters) ? 0 : 1;
     ga.group = plan.distributed ? plan.shards : 1;
     // a shard's partial Gram keeps its lo half: it goes into a sum
     ga.gram_halves = (ga.aa_plain && !plan.distributed) ? 1 : 2;

@@ -118,12 +118,15 @@ def test_bf16_step_batch(gpu_lib, nesterov):
         assert bf16_ulp_diff(np64(W[i]), expect).max() <= 1
 
 
-@pytest.mark.parametrize("iters,coeffs", [(1, None), (2, None), (7, None), (3, (2.0, -1.5, 0.5))])
+@pytest.mark.parametrize("iters,coeffs", [(1, None), (2, None), (7, None), (3, (2.0, -1.5, 0.5)),
+                                          (10, None), (12, None), (13, None), (20, None), (40, None)])
 def test_bf16_step_iters_and_coeffs(gpu_lib, iters, coeffs):
     """muon_step with other iteration counts (iters = 1: the first B X, which
     applies the normalization, is also the one that writes the weights) and
     user coefficients, against the oracle with the same (float32-rounded)
-    coefficients."""
+    coefficients. Up to 12 iterations A*A runs from bf16(A) (the default
+    mode); from 13 on the library switches to the split A (hi + lo), whose
+    error stays inside the bound up to the 64-iteration limit."""
     import muon_newton_schulz_03_amd as mu
     c = mu.DEFAULT_COEFFS if coeffs is None else coeffs
     c32 = tuple(float(np.float32(x)) for x in c)

@@ -160,6 +160,29 @@ muon_status muon_ns_batched(const muon_mat *descs, int32_t n_mats, int32_t iters
 muon_status muon_step(const muon_mat *params, const muon_mat *grads, const muon_mat *moms,
                       int32_t n_mats, float lr, float beta, int32_t nesterov);
 
+/*
+ * muon_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same step, with the same arguments, results and error codes, but with
+ * scratch space taken from a device array inside the library instead of the
+ * caller's workspace (muon_set_workspace is ignored). Nothing is allocated or
+ * freed on the call path.
+ *
+ *   - The array holds MUON_NOALLOC_SCRATCH_BYTES; matrices are processed in
+ *     consecutive groups that fit it. A matrix (or column block) that alone
+ *     needs more returns MUON_ERR_WORKSPACE (a 2048 x 7168 bf16 matrix needs
+ *     about 143 MB, so it fits, one at a time).
+ *   - Each GPU holds its own copy of the array from the first call on it
+ *     until the process ends; its address is looked up on that first call.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (two streams, two threads) race and must be serialized
+ *     by the caller. The array needs no clearing between calls.
+ *   - Phase timing (muon_set_phase_timing) is not recorded for these calls.
+ */
+#define MUON_NOALLOC_SCRATCH_BYTES (256u << 20)
+muon_status muon_step_noalloc(const muon_mat *params, const muon_mat *grads, const muon_mat *moms,
+                              int32_t n_mats, float lr, float beta, int32_t nesterov);
+
 /* Stream for this thread's subsequent calls (a hipStream_t); NULL selects
  * the null stream. */
 muon_status muon_set_stream(void *hip_stream);

@@ -45,8 +45,9 @@ EXPORTED = (
     "muon_ns_batched", "muon_step", "muon_set_stream", "muon_workspace_size",
     "muon_workspace_min_size", "muon_set_workspace", "muon_set_step_options",
     "muon_last_error", "muon_plan_info", "muon_set_phase_timing", "muon_phase_times",
-    "muon_place", "muon_adamw_step",
+    "muon_place", "muon_adamw_step", "muon_step_noalloc",
 )
+MUON_NOALLOC_SCRATCH_BYTES = 256 << 20
 PHASES = ("prep", "norm", "gram", "aa", "bx", "finish", "adamw", "reduce")
 
 
@@ -85,6 +86,8 @@ def load_library(path=LIB_PATH):
         "muon_ns_batched": ([mat_p, ctypes.c_int32, ctypes.c_int32, f3, ctypes.c_uint32], ctypes.c_int),
         "muon_step": ([mat_p, mat_p, mat_p, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_int32],
                       ctypes.c_int),
+        "muon_step_noalloc": ([mat_p, mat_p, mat_p, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                               ctypes.c_int32], ctypes.c_int),
         "muon_set_stream": ([ctypes.c_void_p], ctypes.c_int),
         "muon_workspace_size": ([mat_p, ctypes.c_int32, ctypes.c_uint32, sz], ctypes.c_int),
         "muon_workspace_min_size": ([mat_p, ctypes.c_int32, ctypes.c_uint32, sz], ctypes.c_int),
@@ -297,6 +300,21 @@ def muon_step(params, grads, moms, lr=0.02, beta=0.95, nesterov=False, iters=5, 
     else:
         muon_set_workspace(workspace.data_ptr(), workspace.numel() * workspace.element_size())
     _check(lib().muon_step(mats(W), mats(G), mats(M), len(W), lr, beta, 1 if nesterov else 0))
+
+
+def muon_step_noalloc(params, grads, moms, lr=0.02, beta=0.95, nesterov=False, iters=5,
+                      coeffs=DEFAULT_COEFFS, eps=1e-7, mode=DEFAULT_MODE, col_blocks=None):
+    """muon_step with the library's device scratch instead of a workspace
+    (see muon.h): no device memory is allocated by the library or here."""
+    cb = col_blocks if col_blocks is not None else [1] * len(params)
+    if isinstance(cb, int):
+        cb = [cb] * len(params)
+    W = [mat_of(t, c) for t, c in zip(params, cb)]
+    G = [mat_of(t) for t in grads]
+    M = [mat_of(t) for t in moms]
+    muon_set_stream(None)
+    muon_set_step_options(iters, coeffs, eps, mode)
+    _check(lib().muon_step_noalloc(mats(W), mats(G), mats(M), len(W), lr, beta, 1 if nesterov else 0))
 
 
 def muon_adamw_step(params, grads, exp_avg, exp_avg_sq, lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8,

@@ -100,9 +100,9 @@ muon_status hip_fail(hipError_t e, const char *what) {
 
 // Launch sequence for every group of views that fits the workspace.
 muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, float beta, int nesterov,
-                    const float coeffs[3], float eps) {
+                    const float coeffs[3], float eps, void *workspace) {
   hipStream_t st = g_state.stream;
-  char *ws = static_cast<char *>(g_state.ws);
+  char *ws = static_cast<char *>(workspace);
   const bool bf16 = plan.bf16;
   const int iters = plan.iters;
   const int fin = iters & 1;
@@ -307,6 +307,57 @@ bool need_workspace(Error *err) {
   return true;
 }
 
+// Phase timing off for the duration of a call that may create no events.
+struct TimingOff {
+  bool was;
+  TimingOff() : was(g_timing.on) { g_timing.on = false; }
+  ~TimingOff() { g_timing.on = was; }
+};
+
+// muon_step on the given workspace (the thread's, or with noalloc the
+// library's device scratch, whose address is looked up only after every
+// host-side check has passed).
+muon_status step_impl(const muon_mat *params, const muon_mat *grads, const muon_mat *moms, int32_t n_mats,
+                      float lr, float beta, int32_t nesterov, bool noalloc) {
+  Error err;
+  const uint32_t mode = g_state.mode;
+  if (!validate_descs(params, n_mats, mode, "params", &err) || !validate_descs(grads, n_mats, mode, "grads", &err) ||
+      !validate_descs(moms, n_mats, mode, "moms", &err))
+    return fail(err);
+  if (n_mats > 0 && !validate_step_triplets(params, grads, moms, n_mats, &err)) return fail(err);
+  if (!std::isfinite(lr) || !std::isfinite(beta)) return fail(MUON_ERR_INVALID_ARG, "lr and beta must be finite");
+  if (nesterov != 0 && nesterov != 1) return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
+  if (n_mats == 0) return ok();
+  const muon_mat *arrays[3] = {params, grads, moms};
+  const bool writable[3] = {true, false, true};
+  if (!check_alias(arrays, writable, 3, n_mats, &err)) return fail(err);
+  const char *names[3] = {"params", "grads", "moms"};
+  Plan plan;
+  void *ws = g_state.ws;
+  size_t ws_bytes = g_state.ws_bytes;
+  if (noalloc) {
+    ws_bytes = kNoAllocScratchBytes;
+    if (!build_plan(params, n_mats, g_state.iters, mode, ws_bytes, &plan, &err))
+      return fail(err.status, err.msg + " (muon_step_noalloc: the device scratch holds " +
+                                  std::to_string(kNoAllocScratchBytes >> 20) + " MiB)");
+    hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch symbol address");
+    if (!check_workspace_alias(arrays, names, 3, n_mats, ws, ws_bytes, &err)) return fail(err);
+  } else if (!need_workspace(&err) || !check_workspace_alias(arrays, names, 3, n_mats, ws, ws_bytes, &err) ||
+             !build_plan(params, n_mats, g_state.iters, mode, ws_bytes, &plan, &err)) {
+    return fail(err);
+  }
+  Sources src;
+  src.W = params;
+  src.G = grads;
+  src.M = moms;
+  if (noalloc) {
+    TimingOff off;
+    return execute(plan, src, true, lr, beta, nesterov, g_state.coeffs, g_state.eps, ws);
+  }
+  return execute(plan, src, true, lr, beta, nesterov, g_state.coeffs, g_state.eps, ws);
+}
+
 }  // namespace
 
 extern "C" {
@@ -331,34 +382,17 @@ muon_status muon_ns_batched(const muon_mat *descs, int32_t n_mats, int32_t iters
     return fail(err);
   Sources src;
   src.data = descs;
-  return execute(plan, src, false, 0.f, 0.f, 0, cf, g_state.eps);
+  return execute(plan, src, false, 0.f, 0.f, 0, cf, g_state.eps, g_state.ws);
 }
 
 muon_status muon_step(const muon_mat *params, const muon_mat *grads, const muon_mat *moms, int32_t n_mats,
                       float lr, float beta, int32_t nesterov) {
-  Error err;
-  const uint32_t mode = g_state.mode;
-  if (!validate_descs(params, n_mats, mode, "params", &err) || !validate_descs(grads, n_mats, mode, "grads", &err) ||
-      !validate_descs(moms, n_mats, mode, "moms", &err))
-    return fail(err);
-  if (n_mats > 0 && !validate_step_triplets(params, grads, moms, n_mats, &err)) return fail(err);
-  if (!std::isfinite(lr) || !std::isfinite(beta)) return fail(MUON_ERR_INVALID_ARG, "lr and beta must be finite");
-  if (nesterov != 0 && nesterov != 1) return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
-  if (n_mats == 0) return ok();
-  const muon_mat *arrays[3] = {params, grads, moms};
-  const bool writable[3] = {true, false, true};
-  if (!check_alias(arrays, writable, 3, n_mats, &err)) return fail(err);
-  const char *names[3] = {"params", "grads", "moms"};
-  Plan plan;
-  if (!need_workspace(&err) ||
-      !check_workspace_alias(arrays, names, 3, n_mats, g_state.ws, g_state.ws_bytes, &err) ||
-      !build_plan(params, n_mats, g_state.iters, mode, g_state.ws_bytes, &plan, &err))
-    return fail(err);
-  Sources src;
-  src.W = params;
-  src.G = grads;
-  src.M = moms;
-  return execute(plan, src, true, lr, beta, nesterov, g_state.coeffs, g_state.eps);
+  return step_impl(params, grads, moms, n_mats, lr, beta, nesterov, false);
+}
+
+muon_status muon_step_noalloc(const muon_mat *params, const muon_mat *grads, const muon_mat *moms, int32_t n_mats,
+                              float lr, float beta, int32_t nesterov) {
+  return step_impl(params, grads, moms, n_mats, lr, beta, nesterov, true);
 }
 
 muon_status muon_set_stream(void *hip_stream) {

@@ -146,4 +146,10 @@ hipError_t launch_adamw(const AdamArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_tri_pack(const GemmArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_tri_reduce(const GemmArgs &a, bool bf16, hipStream_t s);
 
+// Allocation-free entry point (scratch.hip): the device address of this
+// device's scratch array of kNoAllocScratchBytes, looked up on the first call
+// per device (with that device current) and cached.
+constexpr size_t kNoAllocScratchBytes = size_t(256) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace muon

@@ -132,6 +132,20 @@ def test_workspace_overlap_rejected(lib):
         mu.muon_set_workspace(None, 0)
 
 
+def test_noalloc_rejects_what_the_scratch_cannot_hold(lib):
+    """muon_step_noalloc plans against its fixed device scratch before any HIP
+    call: a matrix whose workspace alone exceeds it is rejected on the host."""
+    W, G, M = desc(7168, 18432, ptr=FAKE), desc(7168, 18432, ptr=FAKE * 2), desc(7168, 18432, ptr=FAKE * 3)
+    assert mu.muon_workspace_min_size([W]) > mu.MUON_NOALLOC_SCRATCH_BYTES
+    st = lib.muon_step_noalloc(mu.mats([W]), mu.mats([G]), mu.mats([M]), 1, 0.02, 0.95, 0)
+    assert st == mu.MUON_ERR_WORKSPACE
+    assert "scratch" in mu.muon_last_error()
+    # the other host-side checks come first, as in muon_step
+    assert lib.muon_step_noalloc(mu.mats([W]), mu.mats([G]), mu.mats([M]), 1, float("nan"), 0.95, 0) \
+        == mu.MUON_ERR_INVALID_ARG
+    assert lib.muon_step_noalloc(mu.mats([W]), mu.mats([W]), mu.mats([M]), 1, 0.02, 0.95, 0) == mu.MUON_ERR_ALIAS
+
+
 def test_alias_exact_for_interleaved_views(lib):
     # two column blocks of one 8 x 64 bf16 buffer do not overlap element-wise
     left = desc(8, 32, ld=64)

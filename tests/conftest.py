@@ -22,3 +22,19 @@ def gpu_lib():
     import muon_newton_schulz_03_amd as m
     m.load_library()
     return m
+
+
+@pytest.fixture(autouse=True)
+def output_guards(request):
+    """GPU tests: after the test, every buffer made by gpu_util.padded() must
+    still hold its fill in the guard rows around the view and in the pitch
+    padding (nothing was written outside an output)."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    import gpu_util
+    gpu_util.clear_guards()
+    yield
+    import torch
+    torch.cuda.synchronize()
+    gpu_util.check_guards()

@@ -285,3 +285,32 @@ def test_aa_modes(gpu_lib):
     print(f"A*A modes relF {err}")
     assert err["plain"] <= BF16_TOL and err["split"] <= BF16_TOL
     assert err["split"] < err["plain"]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_checkpoint_resume_bitwise(gpu_lib, dtype):
+    """The library carries no state between steps beyond W and M: two steps
+    in a row equal, bit for bit, one step, a checkpoint of W and M through
+    host memory, a workspace overwritten with NaN, and the second step from
+    the restored buffers."""
+    import muon_newton_schulz_03_amd as mu
+    shapes = [(300, 520), (520, 300), (768, 2048)] if dtype == torch.bfloat16 else [(64, 128), (100, 37)]
+    G1 = [rand(s, dtype, 600 + i, std=1e-3)[1] for i, s in enumerate(shapes)]
+    G2 = [rand(s, dtype, 700 + i, std=1e-3)[1] for i, s in enumerate(shapes)]
+    M0 = [rand(s, dtype, 800 + i, std=1e-2)[1] for i, s in enumerate(shapes)]
+    W0 = [rand(s, dtype, 900 + i, std=0.02)[1] for i, s in enumerate(shapes)]
+    W, M = [t.clone() for t in W0], [t.clone() for t in M0]
+    gpu_lib.muon_step(W, G1, M)
+    gpu_lib.muon_step(W, G2, M)
+    Wr, Mr = [t.clone() for t in W0], [t.clone() for t in M0]
+    gpu_lib.muon_step(Wr, G1, Mr)
+    torch.cuda.synchronize()
+    ckW, ckM = [t.cpu() for t in Wr], [t.cpu() for t in Mr]
+    del Wr, Mr
+    mu._ws.buf.fill_(0xFF)  # all-ones bytes: NaN in bf16 and float32
+    Wr, Mr = [t.cuda() for t in ckW], [t.cuda() for t in ckM]
+    gpu_lib.muon_step(Wr, G2, Mr)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(W[i], Wr[i]), shapes[i]
+        assert torch.equal(M[i], Mr[i]), shapes[i]

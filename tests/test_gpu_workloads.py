@@ -22,7 +22,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import bf16_round, bf16_ulp_diff, np64, relF
+from gpu_util import bf16_round, bf16_ulp_diff, check_guards, guarded_copy, np64, relF
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,9 @@ def run_step_checks(gpu_lib, name, sample, aa_mode=None, shapes=None, seed=None)
     from muon_newton_schulz_03_amd.workloads import WORKLOADS, make_inputs
     wl = WORKLOADS[name]
     W, G, M = make_inputs(wl, shapes=shapes, seed=seed)
+    # the written buffers live between NaN guard rows (checked after the test)
+    W = [guarded_copy(t) for t in W]
+    M = [guarded_copy(t) for t in M]
     torch.cuda.synchronize()
     aa = mu.MUON_AA_PLAIN if aa_mode is None else aa_mode
     print(f"{name}: {len(W)} matrices, sample {sample}, A*A mode {aa:#x}", flush=True)
@@ -44,12 +47,13 @@ def run_step_checks(gpu_lib, name, sample, aa_mode=None, shapes=None, seed=None)
     W0 = {i: np64(W[i]) for i in sample}
     mode = mu.MUON_PACK_COST | aa | (mu.MUON_NS_BLOCKWISE if wl.col_blocks > 1 else 0)
     cb = [wl.col_blocks] * len(W)
-    Mc = [t.clone() for t in M]
-    Wz = [torch.zeros_like(t) for t in W]
+    Mc = [guarded_copy(t) for t in M]
+    Wz = [guarded_copy(torch.zeros_like(t)) for t in W]
     gpu_lib.muon_step(Wz, G, Mc, lr=-1.0, beta=wl.beta, iters=wl.iters, mode=mode, col_blocks=cb,
                       max_workspace_bytes=WS_CAP)
     torch.cuda.synchronize()
     O = {i: np64(Wz[i]) for i in sample}
+    check_guards(release=Wz)
     del Wz
     worst = 0.0
     for i in sample:
@@ -60,6 +64,7 @@ def run_step_checks(gpu_lib, name, sample, aa_mode=None, shapes=None, seed=None)
         assert err <= 2e-2, (i, err)
         assert bf16_ulp_diff(np64(Mc[i]), bf16_round(M_ref)).max() <= 1
     print(f"{name}: worst O relF {worst:.3e}", flush=True)
+    check_guards(release=Mc)
     del Mc
     gpu_lib.muon_step(W, G, M, lr=LR32, beta=BETA32, iters=wl.iters, mode=mode, col_blocks=cb,
                       max_workspace_bytes=WS_CAP)

@@ -61,7 +61,100 @@ def parse():
     p.add_argument("--place-ranks", type=int, default=0,
                    help="also place the matrices on R simulated data-parallel ranks, round robin "
                         "vs LPT, with costs measured per matrix shape (0 = off)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (3 times) and exit: the reference "
+                        "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return p.parse_args()
+
+
+class Sampler:
+    """Socket power and shader clock sampled from sysfs (hwmon power1_input,
+    pp_dpm_sclk) every few milliseconds in a background thread while the
+    timed steps run. Reads files only; makes no GPU call."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        dev = "/sys/class/drm/card0/device"
+        pw = glob.glob(dev + "/hwmon/hwmon*/power1_input")
+        self.pw = pw[0] if pw else None
+        self.sclk = dev + "/pp_dpm_sclk" if os.path.exists(dev + "/pp_dpm_sclk") else None
+        self.period = period_s
+        self.w, self.mhz = [], []
+        self.stop = False
+        self.th = threading.Thread(target=self.run, daemon=True)
+
+    def read_sclk(self):
+        with open(self.sclk) as f:
+            for line in f:
+                if "*" in line:
+                    return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        return None
+
+    def run(self):
+        while not self.stop:
+            try:
+                if self.pw:
+                    with open(self.pw) as f:
+                        self.w.append(int(f.read()) / 1e6)
+                if self.sclk:
+                    v = self.read_sclk()
+                    if v:
+                        self.mhz.append(v)
+            except (OSError, ValueError):
+                pass
+            time.sleep(self.period)
+
+    def __enter__(self):
+        self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop = True
+        self.th.join()
+
+    def summary(self):
+        out = {"source": "sysfs hwmon power1_input and pp_dpm_sclk, sampled every 5 ms over the timed steps",
+               "samples": len(self.w)}
+        if self.w:
+            out["avg_w"] = round(sum(self.w) / len(self.w), 1)
+            out["max_w"] = round(max(self.w), 1)
+        if self.mhz:
+            out["sclk_mhz_avg"] = round(sum(self.mhz) / len(self.mhz), 1)
+        cap = None
+        if self.pw:
+            try:
+                with open(self.pw.replace("power1_input", "power1_cap")) as f:
+                    cap = int(f.read()) / 1e6
+            except (OSError, ValueError):
+                cap = None
+        out["cap_w"] = cap
+        return out
+
+
+def environment():
+    """Host, runtime and device facts recorded beside the numbers."""
+    import platform
+    import torch
+    env = {"host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+           "python": platform.python_version(), "torch": torch.__version__, "hip": torch.version.hip}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    if torch.cuda.is_available():
+        pr = torch.cuda.get_device_properties(0)
+        env["device"] = pr.name
+        env["gcn_arch"] = getattr(pr, "gcnArchName", None)
+        env["compute_units"] = pr.multi_processor_count
+    try:
+        from threadpoolctl import threadpool_info
+        env["blas"] = [{"api": i.get("internal_api"), "threads": i.get("num_threads"), "version": i.get("version")}
+                       for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:
+        env["blas"] = None
+    return env
 
 
 def cpu_baseline(wl, budget_s, col_blocks=None):
@@ -199,6 +292,17 @@ def recorded_traffic(workload, kernel):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {args.calibrate_copy} MiB x 3", flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU path is not part of this build)", file=sys.stderr)
@@ -256,13 +360,14 @@ def main():
     # current stream), besides the wall clock around the whole timed region
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for k in range(args.steps):
-        step()
-        ev[k + 1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with Sampler() as sampler:
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for k in range(args.steps):
+            step()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     per_step = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps))
     phases = mu.muon_phase_times() if timing else None
     mu.muon_set_phase_timing(False)
@@ -303,6 +408,8 @@ def main():
         "step_ms": {"median": round(statistics.median(per_step), 3),
                     "p90": round(per_step[math.ceil(0.9 * len(per_step)) - 1], 3),
                     "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
+        "power": sampler.summary(),
+        "env": environment(),
         "tflops_nominal": round(tflops_nom, 2),
         "pct_peak_alg": round(100 * tflops_alg / PEAK_BF16_TFLOPS, 2),
         "pct_peak_nominal": round(100 * tflops_nom / PEAK_BF16_TFLOPS, 2),
@@ -337,6 +444,10 @@ def main():
             "flops_per_launch": fl_launch,
             "avg_launch_ms": round(avg_ms, 4),
         }
+        mhz = out["power"].get("sclk_mhz_avg")
+        if mhz:
+            # the same work against the peak at the shader clock measured during the run
+            out["roofline"]["frac_at_measured_clock"] = round(ach / (256 * 4096 * mhz * 1e6 / 1e12), 4)
         pb = acc.prep_bytes(wl.shapes, 2 if wl.dtype == "bf16" else 4,
                             transposed=wl.dtype == "bf16" and wl.iters > 0)
         out["prep_gbs"] = round(pb / (per_step["prep"][0] * 1e-3) / 1e9, 1) if per_step["prep"][0] > 0 else None
@@ -366,6 +477,9 @@ def main():
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, col_blocks=blocks)
+        # the sample's rate stands for the whole workload: the CPU time one
+        # full step would take at that rate
+        out["cpu_baseline"]["extrapolated_step_s"] = round(f_alg / (out["cpu_baseline"]["value"] * 1e12), 1)
     print(json.dumps(out), flush=True)
 
 

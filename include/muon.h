@@ -123,13 +123,16 @@ typedef struct muon_mat {
  * "2. Newton-Schulz distribuído"): each matrix (rows <= cols; pass a tall
  * matrix transposed) is split into P = col_blocks column shards X_p, every
  * matrix of the call with the same P. Per iteration each shard forms its
- * partial Gram X_p X_p^T; the partials are exchanged as packed upper
- * triangles ([zh] section "SYRK 和融合的 all-reduce": float32, row i holding
- * columns i .. mp - 1, mp the padded row count) and summed in shard order,
- * standing in for the all-reduce; every shard then forms B from the full A
- * (redundantly, as every rank would) and updates its own columns. The norm
- * is the whole matrix's. The result is the full-matrix Newton-Schulz up to
- * rounding order. Shard partial Grams keep their bf16 lo half.
+ * partial Gram X_p X_p^T; the partials are exchanged as float32 upper
+ * triangles ([zh] section "SYRK 和融合的 all-reduce") and summed in shard
+ * order, standing in for the all-reduce; every shard then forms B from the
+ * full A (redundantly, as every rank would) and updates its own columns. The
+ * norm is the whole matrix's. The result is the full-matrix Newton-Schulz up
+ * to rounding order. bf16: the Gram kernel writes each partial tile by tile,
+ * straight from its accumulators, as the upper 256 x 256 tiles in float32
+ * (tile-packed), and the sum, 16 bytes per access, leaves as the bf16 A that
+ * every shard of the matrix reads; float32: packed rows (row i holding
+ * columns i .. mp - 1, mp the padded row count).
  *   eps     taken from muon_set_step_options (default 1e-7).
  * n_mats == 0 is a no-op returning MUON_OK.
  */

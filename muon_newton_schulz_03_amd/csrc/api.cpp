@@ -125,8 +125,9 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
     ga.eps = eps;
     ga.aa_plain = ((plan.mode & MUON_AA_SPLIT) || iters > kPlainMaxIters) ? 0 : 1;
     ga.group = plan.distributed ? plan.shards : 1;
-    // a shard's partial Gram keeps its lo half: it goes into a sum
-    ga.gram_halves = (ga.aa_plain && !plan.distributed) ? 1 : 2;
+    // halves of A written (by the Gram, or in distributed mode by the sum)
+    ga.gram_halves = ga.aa_plain ? 1 : 2;
+    ga.tri_out = (plan.distributed && bf16) ? 1 : 0;
     ga.remap = 1;
     int32_t view_begin = 0;
     for (size_t s = 0; s < ch.segs.size(); ++s) {
@@ -251,25 +252,37 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       ga.persistent = 0;
       if (e != hipSuccess) return hip_fail(e, "gram launch");
       if (plan.distributed) {
-        // the all-reduce of the partial Grams, simulated on this GPU: one
-        // workgroup per row of each view (pack) or of each matrix (reduce)
-        int64_t t = 0;
-        for (size_t s = 0; s < ch.segs.size(); ++s) {
-          ga.seg[s].tiles_per_view = int32_t(ch.segs[s].mp);
-          ga.seg[s].tile_begin = int32_t(t);
-          t += ch.segs[s].mp * ch.segs[s].count;
+        // the all-reduce of the partial Grams, simulated on this GPU
+        auto per_matrix = [&](int64_t tile) {  // tile: edge of the tiles summed
+          int64_t t = 0;
+          for (size_t s = 0; s < ch.segs.size(); ++s) {
+            const int64_t tt = ch.segs[s].mp / tile;
+            ga.seg[s].tiles_per_view = int32_t(tt * (tt + 1) / 2 * (bf16 ? 4 : 1));
+            ga.seg[s].tile_begin = int32_t(t);
+            t += ga.seg[s].tiles_per_view * (ch.segs[s].count / ga.group);
+          }
+        };
+        if (bf16) {
+          // the Gram wrote tile-packed float32 partials: one workgroup per
+          // quarter of an upper 256 x 256 tile of each matrix
+          per_matrix(kGemmTile);
+          e = timed(kTReduce, st, [&] { return launch_tile_sum(ga, st); });
+          if (e != hipSuccess) return hip_fail(e, "tile sum launch");
+        } else {
+          // one workgroup per row of each view (pack), then per 64 x 64
+          // upper tile of each matrix (sum)
+          int64_t t = 0;
+          for (size_t s = 0; s < ch.segs.size(); ++s) {
+            ga.seg[s].tiles_per_view = int32_t(ch.segs[s].mp);
+            ga.seg[s].tile_begin = int32_t(t);
+            t += ch.segs[s].mp * ch.segs[s].count;
+          }
+          e = timed(kTReduce, st, [&] { return launch_tri_pack(ga, st); });
+          if (e != hipSuccess) return hip_fail(e, "triangle pack launch");
+          per_matrix(64);
+          e = timed(kTReduce, st, [&] { return launch_tri_reduce(ga, st); });
+          if (e != hipSuccess) return hip_fail(e, "triangle reduce launch");
         }
-        e = timed(kTReduce, st, [&] { return launch_tri_pack(ga, bf16, st); });
-        if (e != hipSuccess) return hip_fail(e, "triangle pack launch");
-        t = 0;
-        for (size_t s = 0; s < ch.segs.size(); ++s) {
-          const int64_t tt = ch.segs[s].mp / 64;
-          ga.seg[s].tiles_per_view = int32_t(tt * (tt + 1) / 2);
-          ga.seg[s].tile_begin = int32_t(t);
-          t += ga.seg[s].tiles_per_view * (ch.segs[s].count / ga.group);
-        }
-        e = timed(kTReduce, st, [&] { return launch_tri_reduce(ga, bf16, st); });
-        if (e != hipSuccess) return hip_fail(e, "triangle reduce launch");
         set_tiles(true);
       }
       // A*A (short K loop as well): persistent workgroups (measured -1.5%)

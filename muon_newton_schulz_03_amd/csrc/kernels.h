@@ -102,7 +102,10 @@ struct GemmArgs {
   float lr;           // muon_step's learning rate (for last)
   int32_t group;      // views per matrix that share one norm and one Gram
                       // (distributed mode: the shards), else 1
-  int32_t gram_halves;// bf16 Gram: 1 writes A hi only, 2 also A lo
+  int32_t gram_halves;// bf16 A: 1 writes A hi only, 2 also A lo
+  int32_t tri_out;    // bf16 distributed mode: the Gram writes the shard's
+                      // float32 partial (tile-packed) instead of A, and A*A
+                      // reads the A of the matrix's first shard
   float a, b, c;
   float r;          // b / c: the A*A kernel adds r A inside its K loop, then scales by c
   float eps;
@@ -137,14 +140,21 @@ hipError_t launch_elem(const ElemArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_norm_finalize(const GemmArgs &a, int views, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &a, int phase, bool bf16, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs &a, bool bf16, hipStream_t s);
-// Distributed mode (dist.hip): pack each shard's Gram into its upper-triangle
-// buffer (tiles_per_view = mp: one workgroup per row of a view); sum the
-// packed buffers of every matrix's shards in shard order and unpack the sum
-// into every shard's A (tiles_per_view = t (t + 1) / 2 upper 64 x 64 tiles
-// per matrix, t = mp / 64, with count / group matrices per segment).
-// tile_begin holds the prefix over segments in both cases.
-hipError_t launch_tri_pack(const GemmArgs &a, bool bf16, hipStream_t s);
-hipError_t launch_tri_reduce(const GemmArgs &a, bool bf16, hipStream_t s);
+// Distributed mode (dist.hip).
+// bf16: the Gram kernel (tri_out) writes each shard's float32 partial into
+// its tile-packed buffer; launch_tile_sum sums the `group` partials of every
+// matrix in shard order into the first shard's A (tiles_per_view =
+// 4 t (t + 1) / 2 per matrix: a quarter of an upper 256 x 256 tile per
+// workgroup, t = mp / 256, count / group matrices per segment).
+// float32: pack each shard's Gram into its row-packed upper triangle
+// (tiles_per_view = mp: one workgroup per row of a view); sum the packed
+// buffers of every matrix's shards in shard order and unpack the sum into
+// every shard's A (tiles_per_view = t (t + 1) / 2 upper 64 x 64 tiles per
+// matrix, t = mp / 64, with count / group matrices per segment).
+// tile_begin holds the prefix over segments in every case.
+hipError_t launch_tile_sum(const GemmArgs &a, hipStream_t s);
+hipError_t launch_tri_pack(const GemmArgs &a, hipStream_t s);
+hipError_t launch_tri_reduce(const GemmArgs &a, hipStream_t s);
 
 // Allocation-free entry point (scratch.hip): the device address of this
 // device's scratch array of kNoAllocScratchBytes, looked up on the first call

@@ -44,6 +44,7 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -648,8 +649,11 @@ void gemm_bf16_kernel(const GemmArgs args) {
     ld = np;
     K = np;
   } else if (PHASE == kAA) {
-    P = Q = reinterpret_cast<const bf16 *>(blk + S.off_ahi);
-    P2 = Q2 = reinterpret_cast<const bf16 *>(blk + S.off_alo);
+    // distributed mode: every shard of a matrix reads the summed A held by
+    // the matrix's first shard
+    const char *ablk = args.tri_out ? S.base + int64_t(ti.view - ti.view % args.group) * S.stride : blk;
+    P = Q = reinterpret_cast<const bf16 *>(ablk + S.off_ahi);
+    P2 = Q2 = reinterpret_cast<const bf16 *>(ablk + S.off_alo);
     ld = mp;
     K = args.aa_plain ? mp : 3 * mp;
   } else {
@@ -894,7 +898,24 @@ void gemm_bf16_kernel(const GemmArgs args) {
   const bool diag = (PHASE != kBX) && ti.I == ti.J;
   float *scale_p = reinterpret_cast<float *>(blk + S.off_scale);
 
-  if (PHASE == kGram) {
+  if (PHASE == kGram && args.tri_out) {
+    // Distributed mode: this shard's partial s' X_p X_p^T leaves in float32,
+    // straight from the accumulators into its tile-packed buffer (layout.h;
+    // block (bi, bj) of wave (wm, wn) is block (4 wm + bi, 2 wn + bj) of the
+    // tile, its quad 2 g + fh from registers 4 g .. 4 g + 3)
+    const float sg = args.first ? scale_p[1] : 1.f;
+    float *dst = reinterpret_cast<float *>(blk + S.off_tri) + int64_t(ti.J * (ti.J + 1) / 2 + ti.I) * kTriTileFloats;
+    for_blocks(acc, [&](f32x16 &a, int bi, int bj) {
+      float *d = dst + ((wm * 4 + bi) * 8 + wn * 2 + bj) * 1024 + fh * 128 + fr * 4;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = a[4 * g + e] * sg;
+        *reinterpret_cast<f32x4 *>(d + g * 256) = v;
+      }
+    });
+  } else if (PHASE == kGram) {
     // A = s' X X^T as bf16 hi + lo. Each output tile passes through LDS once,
     // as A[j][i] (8-byte writes): its rows are the mirror tile (J, I), its
     // transposing reads the tile (I, J); a diagonal tile leaves once,
@@ -907,8 +928,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
         a[r] = __uint_as_float(pack_bf16(x, x - float(bf16(x))));
       }
     });
-    // (the lo half is not needed when A*A runs on bf16(A) alone, unless the
-    // Gram is a shard's partial that goes into a sum)
+    // (the lo half is not needed when A*A runs on bf16(A) alone)
     const int halves = args.gram_halves;
     for (int half = 0; half < halves; ++half) {  // 0: hi (bits 16..31), 1: lo
       bf16 *dst = reinterpret_cast<bf16 *>(blk + (half ? S.off_alo : S.off_ahi));

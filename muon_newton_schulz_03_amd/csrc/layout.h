@@ -20,4 +20,18 @@ __device__ inline int64_t kblk(int64_t r, int64_t c, int64_t cols) {
   return ((r >> 8) * (cols >> 5) + (c >> 5)) * 8192 + (r & 255) * 32 + (c & 31);
 }
 
+// "tile-packed" float32 upper triangle: the message of one shard in the
+// distributed mode (bf16 path). The upper 256 x 256 tiles (I <= J) of an
+// mp x mp symmetric matrix, tile (I, J) at index J (J + 1) / 2 + I, 65536
+// floats each. Inside a tile, 8 x 8 blocks of 32 x 32 in row-major block
+// order (1024 floats each); inside a block, 8 quads of rows (4 q .. 4 q + 3),
+// each stored column by column (32 columns x 4 rows). That is the order in
+// which a wave's 32 x 32 MFMA accumulators leave with 16-byte stores: lane l
+// holds, in registers 4 g .. 4 g + 3, rows 8 g + 4 (l / 32) .. + 3 of column
+// l mod 32, so every store instruction writes 1 KiB contiguously.
+constexpr int kTriTileFloats = 65536;
+__device__ inline int tri_tile_elem(int r, int c) {
+  return ((r >> 5) * 8 + (c >> 5)) * 1024 + ((r & 31) >> 2) * 128 + (c & 31) * 4 + (r & 3);
+}
+
 }  // namespace muon

@@ -59,7 +59,12 @@ Layout view_layout(int64_t mp, int64_t np, bool bf16, bool distributed) {
   L.scale = off;
   off = align_up(off + 4 * sizeof(float), 256);
   L.tri = off;
-  if (distributed) off = align_up(off + size_t(mp) * size_t(mp + 1) / 2 * sizeof(float), 256);
+  if (distributed) {
+    // the shard's partial Gram as sent: bf16 path tile-packed (the upper
+    // 256 x 256 tiles in float32), float32 path packed rows
+    const size_t t = size_t(mp) / 256;
+    off = align_up(off + (bf16 ? t * (t + 1) / 2 * 65536 : size_t(mp) * size_t(mp + 1) / 2) * sizeof(float), 256);
+  }
   L.total = off;
   return L;
 }

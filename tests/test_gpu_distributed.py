@@ -84,38 +84,72 @@ def test_distributed_batch_and_step(gpu_lib):
         assert relF(np64(Wz[i]), O_ref) <= BF16_TOL
 
 
-def test_packed_partial_grams(gpu_lib):
-    """After one iteration each shard's packed buffer holds its partial Gram
-    s^2 X_p X_p^T (upper triangle, row i from column i), and every shard's A
-    is the sum, bitwise identical across shards and symmetric."""
+def untile_upper(buf, mp):
+    """The tile-packed float32 upper triangle of an mp x mp matrix (upper
+    256 x 256 tiles, tile (I, J) at index J (J + 1) / 2 + I; in a tile, 32 x 32
+    blocks in row-major order; in a block, quads of 4 rows stored column by
+    column) as a full matrix whose lower tiles hold NaN."""
+    t = mp // 256
+    out = np.full((mp, mp), np.nan, np.float32)
+    tiles = buf.reshape(-1, 8, 8, 8, 32, 4)  # tile, block row, block col, quad, column, row in quad
+    for J in range(t):
+        for I in range(J + 1):
+            x = tiles[J * (J + 1) // 2 + I]
+            # -> block row, quad, row in quad, block col, column
+            out[I * 256:(I + 1) * 256, J * 256:(J + 1) * 256] = x.transpose(0, 2, 4, 1, 3).reshape(256, 256)
+    return out
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_packed_partial_grams(gpu_lib, split):
+    """After one iteration each shard's buffer holds its partial Gram
+    s^2 X_p X_p^T as tile-packed float32 upper tiles (the message a rank
+    sends), and the matrix's first shard holds A = the sum of the partials in
+    shard order, rounded to bf16 (hi, and lo = the rest when A*A uses both),
+    bit for bit, symmetric, mirrored from the upper tiles."""
     import muon_newton_schulz_03_amd as mu
     shape, P = (300, 1000), 4
     X = rand(shape, torch.bfloat16, 7)
     X0 = np64(X)
-    mode = mu.MUON_NS_DISTRIBUTED | mu.MUON_PACK_RR
+    mode = mu.MUON_NS_DISTRIBUTED | mu.MUON_PACK_RR | (mu.MUON_AA_SPLIT if split else 0)
     gpu_lib.muon_ns_batched([X], iters=1, mode=mode, col_blocks=P)
     torch.cuda.synchronize()
     desc = mu.mat_of(X, P)
     plan = mu.muon_plan_info([desc], iters=1, mode=mode, workspace_bytes=mu._ws.nbytes)
     seg = plan["chunks"][0]["segments"][0]
     L, mp, stride, base = seg["layout"], seg["mp"], seg["stride"], seg["base"]
+    assert mp == 512  # two tile rows: a diagonal and an off-diagonal tile
     buf = mu._ws.buf
     m, w = shape[0], shape[1] // P
     s = 1.0 / (np.linalg.norm(X0) + 1e-7)
-    iu = np.triu_indices(mp)
-    As = []
+    t = mp // 256
+    nfl = t * (t + 1) // 2 * 65536
+    parts = []
     for p in range(P):
         blk = base + p * stride
-        tri = buf[blk + L["tri"]: blk + L["tri"] + mp * (mp + 1) // 2 * 4].view(torch.float32).cpu().numpy()
+        tri = buf[blk + L["tri"]: blk + L["tri"] + nfl * 4].view(torch.float32).cpu().numpy()
+        up = untile_upper(tri, mp)
         Xp = np.zeros((mp, w))
         Xp[:m] = X0[:, p * w:(p + 1) * w]
         part = s * s * (Xp @ Xp.T)
-        assert relF(tri.astype(np.float64), part[iu]) < 1e-4
-        Ah = unblock(buf[blk + L["ahi"]: blk + L["ahi"] + mp * mp * 2].view(torch.bfloat16), mp, mp)
-        Al = unblock(buf[blk + L["alo"]: blk + L["alo"] + mp * mp * 2].view(torch.bfloat16), mp, mp)
-        As.append((Ah.clone(), Al.clone()))
-    for Ah, Al in As:
-        assert torch.equal(Ah, As[0][0]) and torch.equal(Al, As[0][1])
-        assert torch.equal(Ah, Ah.t())
-    A = np64(As[0][0]) + np64(As[0][1])
-    assert relF(A[:m, :m], s * s * (X0 @ X0.T)) < 1e-4
+        iu = np.triu_indices(mp)
+        assert relF(up[iu].astype(np.float64), part[iu]) < 1e-5
+        parts.append(up)
+    # the sum in shard order, in float32, then rounded as the kernel rounds
+    tot = np.zeros((mp, mp), np.float32)
+    for up in parts:
+        tot = tot + up
+    tot = np.triu(tot) + np.triu(tot, 1).T  # symmetrized from the upper triangle
+    hi_ref = torch.from_numpy(tot).to(torch.bfloat16)
+    lo_ref = torch.from_numpy(tot - hi_ref.float().numpy()).to(torch.bfloat16)
+    blk = base
+    Ah = unblock(buf[blk + L["ahi"]: blk + L["ahi"] + mp * mp * 2].view(torch.bfloat16), mp, mp).cpu()
+    assert torch.equal(Ah, Ah.t())
+    assert torch.equal(Ah.view(torch.int16), hi_ref.view(torch.int16))
+    if split:
+        Al = unblock(buf[blk + L["alo"]: blk + L["alo"] + mp * mp * 2].view(torch.bfloat16), mp, mp).cpu()
+        assert torch.equal(Al.view(torch.int16), lo_ref.view(torch.int16))
+        A = np64(Ah) + np64(Al)
+        assert relF(A[:m, :m], s * s * (X0 @ X0.T)) < 1e-5
+    else:
+        assert relF(np64(Ah)[:m, :m], s * s * (X0 @ X0.T)) < 4e-3

@@ -150,10 +150,6 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       g.count = sg.count;
       g.tn = int32_t(sg.np / (bf16 ? kGemmTile : kPadF32));
       g.nparts = int32_t(L.nparts);
-      {
-        const int32_t ti = int32_t(sg.mp / (bf16 ? kGemmTile : kPadF32));
-        g.jblock = ti >= 32 ? 1 : 32 / ti;
-      }
       g.view_begin = view_begin;
       view_begin += sg.count;
     }

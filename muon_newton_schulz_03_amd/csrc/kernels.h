@@ -83,8 +83,6 @@ struct GemmSeg {
   int32_t tn;      // tiles along n (B X phase)
   int32_t nparts;  // partial sums per view
   int32_t view_begin;
-  int32_t jblock;  // B X phase: column panels per tile block
-  int32_t pad_;
 };
 
 struct GemmArgs {

@@ -79,14 +79,15 @@ __device__ inline TileInfo decode_tile(const GemmArgs &a, int tile, bool syrk) {
     while (J * (J + 1) / 2 > u) --J;
     I = u - J * (J + 1) / 2;
   } else {
-    // B X tiles go in blocks of (all row panels) x (jblock column panels):
-    // about 32 consecutive tiles, one XCD's worth, then share every panel of
-    // B and jblock panels of X, so both stay in that XCD's L2
-    const int tI = S.mp / (S.np / S.tn);
-    const int per = tI * S.jblock;
-    const int jb = u / per, r = u - jb * per;
-    I = r % tI;
-    J = jb * S.jblock + r / tI;
+    // B X tiles go in bands of up to 8 row panels, column by column within a
+    // band: 32 consecutive tiles, one XCD's worth, then cover 8 row panels x
+    // 4 column panels and share 8 panels of B and 4 of X^T in that XCD's L2
+    // (a matrix with at most 8 row panels is one band, column by column)
+    const int tJ = S.tn, tI = S.mp / (S.np / tJ);
+    const int band = u / (8 * tJ), r0 = 8 * band, rows = min(8, tI - r0);
+    const int r = u - band * 8 * tJ;
+    I = r0 + r % rows;
+    J = r / rows;
   }
   return {s, view, I, J};
 }

@@ -73,11 +73,35 @@ __device__ inline TileInfo decode_tile(const GemmArgs &a, int tile, bool syrk) {
   const int view = u / S.tiles_per_view;
   u -= view * S.tiles_per_view;
   int I, J;
-  if (syrk) {  // upper triangle, column by column: u = J (J + 1) / 2 + I
-    J = int((sqrtf(8.f * float(u) + 1.f) - 1.f) * 0.5f);
-    while ((J + 1) * (J + 2) / 2 <= u) ++J;
-    while (J * (J + 1) / 2 > u) --J;
-    I = u - J * (J + 1) / 2;
+  if (syrk) {
+    // upper-triangle tiles (I <= J) of the t x t grid. Up to 8 panels (36
+    // tiles, about one XCD's worth): column by column, u = J (J + 1) / 2 + I.
+    // Beyond: in bands of 8 column panels (band b: J in [8 b, 8 b + w)),
+    // within a band row by row, each row's J >= I ascending, so that 32
+    // consecutive tiles cover about 4 row panels x 8 column panels instead
+    // of up to 32 + 2 panels (Kimi dense A*A and Gram: +1.1% per step)
+    const int t = S.mp / (S.np / S.tn);
+    if (t <= 8) {
+      J = int((sqrtf(8.f * float(u) + 1.f) - 1.f) * 0.5f);
+      while ((J + 1) * (J + 2) / 2 <= u) ++J;
+      while (J * (J + 1) / 2 > u) --J;
+      I = u - J * (J + 1) / 2;
+      return {s, view, I, J};
+    }
+    int c0 = 0;
+    while (c0 + 8 < t && u >= (c0 + 8) * (c0 + 9) / 2) c0 += 8;
+    const int w = min(8, t - c0);
+    int v = u - c0 * (c0 + 1) / 2;
+    if (v < c0 * w) {
+      I = v / w;
+      J = c0 + v % w;
+    } else {
+      v -= c0 * w;
+      int i = 0;
+      while (v >= w - i) v -= w - i++;
+      I = c0 + i;
+      J = I + v;
+    }
   } else {
     // B X tiles go in bands of up to 8 row panels, column by column within a
     // band: 32 consecutive tiles, one XCD's worth, then cover 8 row panels x

@@ -741,6 +741,11 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // multiples of 32 rows)
   const int fa = (wm * 128 + fr) * 64, fb = (wn * 64 + fr) * 64;
   const int fx = (fr >> 2) & 3;
+  // A diagonal SYRK tile (I == J) multiplies one row panel by itself: its K
+  // steps load the panel once, and both fragment sets come from that copy
+  // (not in split A*A, whose hi*lo and lo*hi segments pair different halves)
+  const bool dq = PHASE != kBX && __builtin_amdgcn_readfirstlane(
+      int((PHASE == kGram || args.aa_plain) && ti.I == ti.J)) != 0;
   // issue the loads of K step ks_ into its stage (for A*A, K runs over three
   // segments of length mp: hi*hi, hi*lo, lo*hi)
 #define MUON_GLOAD(ks_)                                                              \
@@ -759,14 +764,14 @@ void gemm_bf16_kernel(const GemmArgs args) {
       const uint32_t so_ = uint32_t(k0_ >> 5) * 16384u;                              \
       _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
         load_lds16(ra_, st_ + loff[q], gob[q], so_);                                 \
-        load_lds16(rb_, st_ + kOpBytes + loff[q], gob[q], so_);                      \
+        if (!dq) load_lds16(rb_, st_ + kOpBytes + loff[q], gob[q], so_);             \
       }                                                                              \
     }                                                                                \
   } while (0)
 #define MUON_FRAGS(buf_, ks_, kk_)                                                   \
   do {                                                                               \
     const char *As_ = smem + ((ks_) % kStages) * kStageBytes;                        \
-    const char *Bs_ = As_ + kOpBytes;                                                \
+    const char *Bs_ = dq ? As_ : As_ + kOpBytes;                                     \
     const int ch_ = (((kk_) * 2 + fh) ^ fx) << 4;                                    \
     _Pragma("unroll") for (int bi = 0; bi < 4; ++bi)                                 \
       af[buf_][bi] = *reinterpret_cast<const bf16x8 *>(As_ + fa + bi * 2048 + ch_);  \
@@ -782,10 +787,18 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // s_waitcnt with vmcnt constrained (gfx9 encoding: vmcnt[3:0] and [15:14],
   // expcnt[6:4] and lgkmcnt[11:8] left at their maxima), in the loader waves
   // only: the others have no load in flight that targets LDS, and the
-  // barrier after the loaders' wait publishes their stages to every wave
+  // barrier after the loaders' wait publishes their stages to every wave.
+  // n_ counts the loads of a full step (8 per loader wave); a diagonal tile
+  // issues half of them
+#define MUON_VMCNT(n_) ((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0F70)
 #define MUON_WAIT_VM(n_)                                                             \
   do {                                                                               \
-    if (loader) __builtin_amdgcn_s_waitcnt((((n_) & 15) | (((n_) >> 4) << 14)) | 0x0F70); \
+    if (loader) {                                                                    \
+      if (dq)                                                                        \
+        __builtin_amdgcn_s_waitcnt(MUON_VMCNT((n_) / 2));                            \
+      else                                                                           \
+        __builtin_amdgcn_s_waitcnt(MUON_VMCNT(n_));                                  \
+    }                                                                                \
   } while (0)
   // One K step reads stage ks only: the fragments of its k 0..15 and of its
   // k 16..31 (consumed by the MFMAs at the top of the next step). The loads
@@ -911,6 +924,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #undef MUON_FRAGS
 #undef MUON_MFMA
 #undef MUON_WAIT_VM
+#undef MUON_VMCNT
 #undef MUON_STEP_CORE
 #undef MUON_STEP_BODY
 #undef MUON_STEP

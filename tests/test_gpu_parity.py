@@ -44,8 +44,11 @@ def test_f32_step_64x128(gpu_lib):
     assert relF(W0 - np64(W[0]), W0 - W_ref) <= F32_TOL
 
 
+# (600, 700) and (1100, 577): 10 row panels of 64, so the SYRK tiles run in
+# bands of 8 column panels, the last one 2 wide
 @pytest.mark.parametrize("shape,ld", [((100, 37), 40), ((37, 100), 103), ((1, 50), 50), ((64, 64), 64),
-                                      ((130, 260), 264), ((300, 7), 7), ((65, 65), 66)])
+                                      ((130, 260), 264), ((300, 7), 7), ((65, 65), 66),
+                                      ((600, 700), 704), ((1100, 577), 580)])
 def test_f32_ns_ragged(gpu_lib, shape, ld):
     base, X = rand(shape, torch.float32, 7, ld=ld)
     X0 = np64(X)
@@ -69,9 +72,13 @@ def test_f32_iters(gpu_lib, iters):
 # bf16 path
 # ---------------------------------------------------------------------------
 
+# (2100, 2400): 9 row panels of 256 (B X in a band of 8 row panels and one
+# of 1, the SYRK tiles in a band of 8 column panels and one of 1);
+# (2600, 2305), tall: 10 (last bands 2 wide)
 BF16_SHAPES = [((300, 520), 520), ((520, 300), 304), ((256, 256), 256), ((1, 64), 64), ((64, 1), 8),
                ((1, 96), 96), ((2, 300), 304),
-               ((777, 1030), 1032), ((512, 2048), 2048), ((1030, 777), 777)]
+               ((777, 1030), 1032), ((512, 2048), 2048), ((1030, 777), 777),
+               ((2100, 2400), 2400), ((2600, 2305), 2312)]
 
 
 @pytest.mark.parametrize("shape,ld", BF16_SHAPES)

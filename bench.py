@@ -304,8 +304,8 @@ def main():
         print(f"copied {args.calibrate_copy} MiB x 3", flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU path is not part of this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path is implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
     import muon_newton_schulz_03_amd as mu

@@ -344,7 +344,10 @@ def test_algorithmic_flops_by_enumeration(m, n):
     assert acc.flops_nominal(m, n, 1) == 2 * m * m * n + 2 * m ** 3 + 2 * m * m * n
 
 
-def test_workload_flops_match_survey_table():
+def test_workload_flops_match_hand_counts():
+    """Per-step FLOPs of two workloads, counted by hand from the shapes: the
+    Kimi MoE layer (1152 matrices, 5 iterations) and the blockwise dense
+    matrix (8 column blocks of 7168 x 2304, each oriented to 2304 x 7168)."""
     from muon_newton_schulz_03_amd.workloads import WORKLOADS
     nom, alg = acc.workload_flops(WORKLOADS["kimi_moe_layer"].shapes, 5)
     assert nom / 1e12 == pytest.approx(791.648, abs=1e-3)

@@ -2,8 +2,9 @@
 results must equal muon_step's on the same inputs (same kernels, same
 arithmetic per matrix; only the scratch differs, so equality is bitwise), on
 two calls in a row, the second with fewer and smaller matrices than the
-first, for both precision paths; and its orthogonalized update must meet the
-bf16 bound against the float64 oracle.
+first, for both precision paths; its orthogonalized update must meet the
+bf16 bound against the float64 oracle; and a HIP graph that records it must
+replay bit for bit.
 """
 import numpy as np
 import pytest
@@ -59,3 +60,38 @@ def test_noalloc_matches_muon_step(gpu_lib):
     run_both(mu, second, torch.bfloat16, 22)
     print("noalloc: float32", flush=True)
     run_both(mu, [(64, 128), (100, 37)], torch.float32, 23)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_noalloc_graph_replays(gpu_lib, dtype):
+    """The entry point's purpose: a caller that cannot allocate records the
+    step into a HIP graph (torch.cuda.graph on its own stream) and replays
+    it. Three replays, each after fresh inputs are copied in eagerly and the
+    device synchronized, each bit for bit equal to the eager call."""
+    import muon_newton_schulz_03_amd as mu
+    shapes = [(300, 520), (520, 300), (256, 768)] if dtype == torch.bfloat16 else [(64, 128), (100, 37)]
+    W0, G0, M0 = inputs(shapes, dtype, 31)
+    We, Me = [t.clone() for t in W0], [t.clone() for t in M0]
+    mu.muon_step_noalloc(We, G0, Me, lr=0.02, beta=0.95)  # eager reference (and scratch lookup)
+    torch.cuda.synchronize()
+    Wg, Gg, Mg = [t.clone() for t in W0], [t.clone() for t in G0], [t.clone() for t in M0]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mu.muon_step_noalloc(Wg, Gg, Mg, lr=0.02, beta=0.95)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        mu.muon_step_noalloc(Wg, Gg, Mg, lr=0.02, beta=0.95)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for dst, src in zip(Wg + Mg, W0 + M0):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert torch.equal(Wg[i], We[i]), (rep, shapes[i], "W")
+            assert torch.equal(Mg[i], Me[i]), (rep, shapes[i], "M")
+    mu.muon_set_stream(None)

@@ -841,8 +841,9 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // enter as products with a diagonal matrix: in the K step whose 32 k are
   // the 32 output rows of block row bi_, the Q fragments hold exactly the
   // A (or X) values of those outputs, and D Q adds D_mm Q[m][:] to row m.
-  // The diagonal goes in as bf16 hi + lo parts (hi only for the small lo
-  // half of A). Both k halves are captured at the end of their step.
+  // A*A's (b / c) goes in as bf16 hi + lo parts (hi only for the small lo
+  // half of A); B X's a + B_ii as its lo part only, the hi part being B's
+  // stored diagonal. Both k halves are captured at the end of their step.
 #define MUON_CAPTURE(buf_, bi_, dh_, dl_, lo_)                                       \
   do {                                                                               \
     _Pragma("unroll") for (int bj = 0; bj < kBN; ++bj) {                             \
@@ -905,9 +906,8 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #define MUON_CAP_STEP(bi_, FIRST_)                                                   \
       do {                                                                           \
         const float cv = coef_v[bi_], ch = float(bf16(cv));                          \
-        const bf16x8 dh[2] = {diag_frag(ch, lane, 0), diag_frag(ch, lane, 1)};       \
         const bf16x8 dl[2] = {diag_frag(cv - ch, lane, 0), diag_frag(cv - ch, lane, 1)}; \
-        MUON_STEP_CORE(ks, FIRST_, MUON_CAP2(bi_, dh, dl, true));                    \
+        MUON_STEP_CORE(ks, FIRST_, MUON_CAP2(bi_, dl, dl, false));                   \
         ++ks;                                                                        \
       } while (0)
       if (cb == 0) {
@@ -995,7 +995,10 @@ void gemm_bf16_kernel(const GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] *= args.c;
     });
-    // The diagonal of B stays in float32 (bdiag); B stores it as zero. In a
+    // The diagonal of B stays in float32 (bdiag); B stores bf16(a + B_ii)
+    // there instead, the hi part of B X's diagonal term (a + B_ii) X, so that
+    // the B X K loop adds it with the rest of the product and only the lo
+    // part goes in as an extra diagonal product. In a
     // diagonal tile, block (bi, bj) of wave (wm, wn) covers rows
     // 128 wm + 32 bi and columns 64 wn + 32 bj, so the waves with
     // wn / 2 == wm hold diagonal elements, in their blocks with
@@ -1013,7 +1016,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
         for (int r = 0; r < 16; ++r) x = r == rr ? a[r] : x;
         if (holder) bdiag[i0 + wm * 128 + bi * 32 + fr] = x;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) a[r] = (holder && r == rr) ? 0.f : a[r];
+        for (int r = 0; r < 16; ++r) a[r] = (holder && r == rr) ? args.a + x : a[r];
       });
     }
     for_blocks(acc, [&](f32x16 &a, int, int) {

@@ -211,11 +211,14 @@ def test_bf16_symmetric_intermediates(gpu_lib, split):
     for T in (Ah, B):
         assert torch.equal(T, T.t())
     assert np.all(A[m:, :] == 0) and np.all(A[:, m:] == 0)
-    # B is stored with a zero diagonal; its diagonal is kept in float32
-    assert torch.all(torch.diagonal(B) == 0)
+    # B's diagonal is kept in float32 (bdiag); B itself stores bf16(a + B_ii)
+    # there, the hi part of B X's diagonal term (a + B_ii) X
     off = seg["base"] + L["bdiag"]
-    bdiag = buf[off: off + mp * 4].view(torch.float32).cpu().numpy().astype(np.float64)
-    Bfull = np64(B) + np.diag(bdiag)
+    bd32 = buf[off: off + mp * 4].view(torch.float32).cpu()
+    a32 = torch.tensor(3.4445, dtype=torch.float32)
+    assert torch.equal(torch.diagonal(B).cpu().view(torch.int16), (a32 + bd32).to(torch.bfloat16).view(torch.int16))
+    bdiag = bd32.numpy().astype(np.float64)
+    Bfull = np64(B) - np.diag(np.diag(np64(B))) + np.diag(bdiag)
     Bdev = -4.7750 * A + 2.0315 * (A @ A)   # from the device's own A
     Bref = -4.7750 * Aref + 2.0315 * (Aref @ Aref)
     print(f"B relF vs device A {relF(Bfull[:m, :m], Bdev[:m, :m]):.3e}, vs exact {relF(Bfull[:m, :m], Bref):.3e}")

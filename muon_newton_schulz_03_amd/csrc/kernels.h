@@ -19,6 +19,7 @@ namespace muon {
 
 constexpr int kSegsMax = 8;
 constexpr int kElemViewsMax = 16;
+constexpr int kElemTilesPerGroup = 4;  // element-wise launches: 64x64 tiles per workgroup
 
 enum ElemKind : int32_t {
   kPrepNs = 0,    // X0 = data

@@ -94,6 +94,22 @@ int persistent_slots() {
   return (cus / 8) * 8;
 }
 
+// Persistent launch of `grid` workgroups over a's tiles (phase: whose K
+// loop), if there are more tiles than workgroups: the XCDs' tile ranges
+// balanced by estimated time (xcd_ranges).
+void set_persistent(GemmArgs &a, int phase, int grid) {
+  a.persistent = (grid > 0 && a.total_tiles > grid) ? grid : 0;
+  if (!a.persistent) return;
+  int64_t tiles[kSegsMax], ksteps[kSegsMax];
+  for (int s = 0; s < a.nseg; ++s) {
+    const GemmSeg &g = a.seg[s];
+    tiles[s] = int64_t(g.tiles_per_view) * g.count;
+    const int64_t k = phase == kGram ? g.np : phase == kAA ? (a.aa_plain ? g.mp : 3 * g.mp) : g.mp;
+    ksteps[s] = k / 32;
+  }
+  xcd_ranges(tiles, ksteps, a.nseg, a.xcd_begin);
+}
+
 muon_status hip_fail(hipError_t e, const char *what) {
   return fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -243,7 +259,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       set_tiles(true);
       // Gram: persistent workgroups, one per CU, each looping over tiles of
       // its XCD's range (measured -0.8% against one workgroup per tile)
-      ga.persistent = (slots > 0 && ga.total_tiles > slots) ? slots : 0;
+      set_persistent(ga, kGram, slots);
       e = timed(kTGram, st, [&] { return launch_gemm(ga, kGram, bf16, st); });
       ga.persistent = 0;
       if (e != hipSuccess) return hip_fail(e, "gram launch");
@@ -282,7 +298,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
         set_tiles(true);
       }
       // A*A (short K loop as well): persistent workgroups (measured -1.5%)
-      ga.persistent = (slots > 0 && ga.total_tiles > slots) ? slots : 0;
+      set_persistent(ga, kAA, slots);
       e = timed(kTAA, st, [&] { return launch_gemm(ga, kAA, bf16, st); });
       ga.persistent = 0;
       if (e != hipSuccess) return hip_fail(e, "A*A launch");
@@ -290,7 +306,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       // B X (short K loop): persistent workgroups, so that a tile's epilogue
       // stores overlap the next tile's first operand loads. The last one
       // writes the caller's matrices (data <- O or W <- W - lr O).
-      ga.persistent = (slots > 0 && ga.total_tiles > slots) ? slots : 0;
+      set_persistent(ga, kBX, slots);
       ga.last = it == iters - 1 ? 1 : 0;
       ga.lr = lr;
       e = timed(kTBX, st, [&] { return launch_gemm(ga, kBX, bf16, st); });

@@ -96,6 +96,7 @@ struct GemmArgs {
   int32_t remap;    // XCD-aware tile order
   int32_t persistent; // > 0: grid of this many workgroups (a multiple of 8),
                       // each looping over tiles of its XCD's range
+  int32_t xcd_begin[9]; // persistent: XCD x takes tiles [xcd_begin[x], xcd_begin[x + 1])
   int32_t last;       // B X of the last iteration: write the caller's matrices
                       // through each view's OutDesc instead of X'
   float lr;           // muon_step's learning rate (for last)

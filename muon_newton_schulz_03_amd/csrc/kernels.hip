@@ -647,15 +647,14 @@ void gemm_bf16_kernel(const GemmArgs args) {
 
   // Tiles of this workgroup: one (the grid covers every tile), or, in a
   // persistent launch (8 S workgroups, S per XCD), the tiles begin + slot,
-  // begin + slot + S, ... of its XCD's contiguous range, so that the 8 XCDs
-  // each work through their own contiguous part of the tile order.
+  // begin + slot + S, ... of its XCD's contiguous range (the host splits
+  // the tile order into 8 ranges of about equal estimated time), so that
+  // the 8 XCDs each work through their own contiguous part of it.
   int t_cur, t_end, t_step;
   if (args.persistent) {
     const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int q = args.total_tiles >> 3, r = args.total_tiles & 7;
-    const int begin = x * q + min(x, r);
-    t_cur = begin + slot;
-    t_end = begin + q + (x < r ? 1 : 0);
+    t_cur = args.xcd_begin[x] + slot;
+    t_end = args.xcd_begin[x + 1];
     t_step = int(gridDim.x) >> 3;
   } else {
     t_cur = args.remap ? xcd_remap(blockIdx.x, args.total_tiles) : int(blockIdx.x);

@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cmath>
 #include <cstdio>
 #include <numeric>
 #include <queue>
@@ -325,6 +326,32 @@ std::string plan_json(const Plan &p) {
   }
   o << "]}";
   return o.str();
+}
+
+void xcd_ranges(const int64_t *tiles, const int64_t *ksteps, int nseg, int32_t out[9]) {
+  double total = 0;
+  int64_t count = 0;
+  for (int s = 0; s < nseg; ++s) {
+    total += double(tiles[s]) * (double(ksteps[s]) + kTileOverheadSteps);
+    count += tiles[s];
+  }
+  out[0] = 0;
+  out[8] = int32_t(count);
+  for (int x = 1; x < 8; ++x) {
+    const double target = total * x / 8;
+    double acc = 0;
+    int64_t idx = 0;
+    for (int s = 0; s < nseg; ++s) {
+      const double c = double(ksteps[s]) + kTileOverheadSteps;
+      if (acc + double(tiles[s]) * c >= target) {
+        idx += std::min<int64_t>(tiles[s], int64_t(std::llround((target - acc) / c)));
+        break;
+      }
+      acc += double(tiles[s]) * c;
+      idx += tiles[s];
+    }
+    out[x] = int32_t(std::min<int64_t>(std::max<int64_t>(idx, out[x - 1]), count));
+  }
 }
 
 void place(const double *costs, int32_t n, int32_t ranks, uint32_t policy, int32_t *owner,

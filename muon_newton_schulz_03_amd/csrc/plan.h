@@ -122,6 +122,16 @@ bool build_plan(const muon_mat *d, int32_t n, int32_t iters, uint32_t mode, size
 
 std::string plan_json(const Plan &p);
 
+// Persistent launches: the tile order (segment by segment, tiles[s] tiles of
+// ksteps[s] K steps each) split into 8 contiguous ranges, one per XCD, of
+// about equal estimated time, a tile costing its K steps plus a fixed
+// kTileOverheadSteps (prologue and epilogue). out[x] .. out[x + 1] is XCD
+// x's range; out[0] = 0, out[8] = the total. With mixed K (a group of long
+// and short matrices) a split by tile count leaves the XCD that gets the
+// long tiles last.
+constexpr double kTileOverheadSteps = 16.0;
+void xcd_ranges(const int64_t *tiles, const int64_t *ksteps, int nseg, int32_t out[9]);
+
 // Placement of n costs on `ranks` ranks (policy 0: round robin, 1: LPT);
 // writes owner[n] and load[ranks]. Arguments are validated by the caller.
 void place(const double *costs, int32_t n, int32_t ranks, uint32_t policy, int32_t *owner,

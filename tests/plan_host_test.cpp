@@ -7,7 +7,9 @@
 // overlap test and its sweep, the workspace-overlap check, the planner's
 // orientation / padding / blockwise and distributed views / cost order /
 // grouping under a workspace cap / segment limit / tile counts, the layout
-// offsets, the upper-triangle tile enumeration, and the RR / LPT placement.
+// offsets, the upper-triangle tile enumeration, the RR / LPT placement, and
+// the per-XCD tile ranges of persistent launches.
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -233,11 +235,53 @@ static void test_tiles_and_place() {
   CHECK(owner[0] == 0 && owner[1] == 1 && owner[2] == 2);
 }
 
+// Per-XCD tile ranges of a persistent launch: contiguous, monotone, covering
+// every tile; equal tile costs give the count split (to within one tile);
+// mixed K gives each XCD about an eighth of the estimated time.
+static std::vector<int32_t> check_ranges(const std::vector<int64_t> &tiles, const std::vector<int64_t> &ksteps) {
+  int32_t r[9];
+  xcd_ranges(tiles.data(), ksteps.data(), int(tiles.size()), r);
+  int64_t n = 0;
+  double total = 0, biggest = 0;
+  std::vector<double> cost;
+  for (size_t s = 0; s < tiles.size(); ++s) {
+    const double c = double(ksteps[s]) + kTileOverheadSteps;
+    n += tiles[s];
+    for (int64_t t = 0; t < tiles[s]; ++t) cost.push_back(c);
+    total += double(tiles[s]) * c;
+    if (tiles[s] && c > biggest) biggest = c;
+  }
+  CHECK(r[0] == 0 && r[8] == n);
+  double worst = 0;
+  for (int x = 0; x < 8; ++x) {
+    CHECK(r[x] <= r[x + 1]);
+    double c = 0;
+    for (int32_t t = r[x]; t < r[x + 1]; ++t) c += cost[size_t(t)];
+    worst = c > worst ? c : worst;
+  }
+  CHECK(worst <= total / 8 + biggest + 1e-9);  // at most one tile above an even split
+  return std::vector<int32_t>(r, r + 9);
+}
+
+static void test_xcd_ranges() {
+  // uniform: the count split
+  const auto u = check_ranges({1152 * 224}, {64});
+  for (int x = 0; x <= 8; ++x) CHECK(std::llabs(int64_t(u[size_t(x)]) - int64_t(1152) * 224 * x / 8) <= 1);
+  // a Qwen3-block-like B X launch: 256 tiles of 64 K steps first, then 32
+  // of 16 and 9216 of 24; split by count, the first XCD would get all the
+  // long tiles and 17% more than an eighth of the time
+  const auto m = check_ranges({256, 32, 9216}, {64, 16, 24});
+  CHECK(m[1] < 9504 / 8);
+  check_ranges({3, 1, 5}, {128, 8, 24});  // fewer tiles than XCDs
+  check_ranges({0, 40}, {64, 24});        // an empty segment
+}
+
 int main() {
   test_validation();
   test_overlap();
   test_plan();
   test_tiles_and_place();
+  test_xcd_ranges();
   std::printf("plan host test: %d checks passed\n", g_checks);
   return 0;
 }

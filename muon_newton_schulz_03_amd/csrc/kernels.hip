@@ -367,7 +367,7 @@ constexpr int kWaves = 8;                        // two per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kBN = 2;                           // 32-column accumulator blocks per wave (wave tile 128 x 64)
 constexpr int kLoaders = 4;                      // waves 0..3, one per SIMD, issue every operand load
-constexpr int kBxRot = 4;                         // B X: K-loop offset per row tile, in K steps
+constexpr int kBxRot = 1;                         // B X: K-loop offset per row tile, in K steps
 
 // ---------------------------------------------------------------------------
 // Epilogues. After the K loop the LDS ring holds one 256 x 256 bf16 (128 KiB)
@@ -724,8 +724,10 @@ void gemm_bf16_kernel(const GemmArgs args) {
   // panel of X^T then read different k at any moment instead of the same 32
   // (which loads the same lines from 8 CUs at once), yet close enough
   // together that the panel's slabs are still in L2 for the next row tile.
-  // Measured per row-tile offset in K steps against 4 (k-blocked operands):
-  // 8 (the tile's own diagonal block) +4%; 0, 1 and 2 within 0.5%.
+  // Measured per row-tile offset in K steps (Kimi MoE batch, B X per step
+  // and its reads per launch): 4: 325.4 ms, 44.6 GB; 2: 326.0 ms, 39.6 GB;
+  // 1: 324.3 ms, 37.6 GB; 0: 328.1 ms, 36.4 GB (8, the tile's own diagonal
+  // block, was 4% slower than 4 in an earlier kernel).
   const int krot = PHASE == kBX ? ti.I * kBxRot * kBK : 0;
 
   // B X: a + diag(B) for the row this lane supplies in each block row

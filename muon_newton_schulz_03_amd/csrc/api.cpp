@@ -180,7 +180,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
       ga.total_tiles = int32_t(t);
     };
 
-    // element-wise launches, up to kElemViewsMax views each
+    // element-wise launches, up to kPrepViewsMax views each
     auto elem_pass = [&](bool prep) -> muon_status {
       ElemArgs ea{};
       ea.kind = prep ? (step ? kPrepStep : kPrepNs) : (step ? kFinishStep : kFinishNs);
@@ -240,7 +240,7 @@ muon_status execute(const Plan &plan, const Sources &src, bool step, float lr, f
         e.tile_begin = tiles;
         tiles += int32_t(tr * tcn);
         ea.nv++;
-        if (ea.nv == kElemViewsMax) {
+        if (ea.nv == kPrepViewsMax) {
           muon_status s = flush();
           if (s != MUON_OK) return s;
         }
@@ -602,7 +602,7 @@ muon_status muon_adamw_step(const muon_mat *params, const muon_mat *grads, const
   for (int32_t i = 0; i < n_mats; ++i) {
     const int64_t cpr = (params[i].cols + 7) / 8;
     const int64_t chunks = params[i].rows * cpr;
-    if (a.nv == kElemViewsMax || int64_t(a.total_chunks) + chunks > (int64_t(1) << 31) - 256) {
+    if (a.nv == kAdamViewsMax || int64_t(a.total_chunks) + chunks > (int64_t(1) << 31) - 256) {
       muon_status s = flush();
       if (s != MUON_OK) return s;
     }

@@ -975,17 +975,19 @@ void gemm_bf16_kernel(const GemmArgs args) {
     const float sg = args.first ? scale_p[1] : 1.f;
     for_blocks(acc, [&](f32x16 &a, int, int) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = a[r] * sg;
-        a[r] = __uint_as_float(pack_bf16(x, x - float(bf16(x))));
-      }
+      for (int r = 0; r < 16; ++r) a[r] *= sg;
     });
-    // (the lo half is not needed when A*A runs on bf16(A) alone)
+    // hi = bf16(A) first, rounded on the way into LDS; the lo half A - hi
+    // (only when A*A runs on the split A) is formed in place afterwards
     const int halves = args.gram_halves;
-    for (int half = 0; half < halves; ++half) {  // 0: hi (bits 16..31), 1: lo
+    for (int half = 0; half < halves; ++half) {  // 0: hi, 1: lo
       bf16 *dst = reinterpret_cast<bf16 *>(blk + (half ? S.off_alo : S.off_ahi));
-      const int shift = half ? 0 : 16;
-      fill_tile<true>(smem, acc, ec, shift);
+      if (half)
+        for_blocks(acc, [&](f32x16 &a, int, int) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a[r] -= float(bf16(a[r]));
+        });
+      fill_tile_trans_f32(smem, acc, ec);
       lds_barrier();
       if (diag) {
         tile_store_sym(smem, dst, mp, i0, j0, tid);
@@ -1025,11 +1027,7 @@ void gemm_bf16_kernel(const GemmArgs args) {
         for (int r = 0; r < 16; ++r) a[r] = (holder && r == rr) ? args.a + x : a[r];
       });
     }
-    for_blocks(acc, [&](f32x16 &a, int, int) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) a[r] = __uint_as_float(pack_bf16(0.f, a[r]));
-    });
-    fill_tile<true>(smem, acc, ec, 0);
+    fill_tile_trans_f32(smem, acc, ec);
     lds_barrier();
     if (diag) {
       tile_store_sym(smem, Bm, mp, i0, j0, tid);
